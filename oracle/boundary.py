@@ -1,0 +1,85 @@
+"""Oracle for the document-id / segment-boundary calls (test infrastructure).
+
+Follows the "nemo_automodel.components.models.glm5_next.cp" page, API entries
+``doc_ids_from_cu_seqlens``, ``doc_ids_from_seq_lens`` and
+``segment_cu_seqlens``.  Pure Python/numpy, written for reading, not speed.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PAD_DOC_ID = -1000
+
+
+def doc_ids_from_cu_seqlens(cu_seqlens, seq_len: int) -> np.ndarray:
+    """Cumulative document boundaries -> per-position document ids ``[1, seq_len]``.
+
+    glm5_next.cp page, ``doc_ids_from_cu_seqlens``: "cumulative document
+    boundaries to ids [1, sequence]".  ``cu_seqlens`` has N+1 entries
+    (``BlockdiagCpModelState.packed_cu_seqlens`` shape ``[num_documents + 1]``).
+
+    Reading (the page does not say): document i, covering ``[cu[i], cu[i+1])``,
+    gets id ``i + 1``; every other position is padding (-1000).  ``cu`` must be
+    non-decreasing with ``0 <= cu[0]`` and ``cu[N] <= seq_len``; anything else
+    raises ``ValueError`` instead of being truncated.
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if len(cu) < 1:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if seq_len < 0:
+        raise ValueError("negative seq_len")
+    if cu[0] < 0 or cu[-1] > seq_len:
+        raise ValueError("cu_seqlens outside [0, seq_len]")
+    for i in range(len(cu) - 1):
+        if cu[i + 1] < cu[i]:
+            raise ValueError("cu_seqlens is not non-decreasing")
+    ids = [PAD_DOC_ID] * seq_len
+    for i in range(len(cu) - 1):
+        for p in range(cu[i], cu[i + 1]):
+            ids[p] = i + 1
+    return np.asarray(ids, dtype=np.int32).reshape(1, seq_len)
+
+
+def doc_ids_from_seq_lens(seq_lens, seq_len: int, padding_value: int = PAD_DOC_ID) -> np.ndarray:
+    """Per-document lengths ``[batch, documents]`` -> ids ``[batch, seq_len]``.
+
+    glm5_next.cp page, ``doc_ids_from_seq_lens`` (padding id defaults to -1000);
+    the inkling2 ``unpack_row_layout`` entry says the length table itself is
+    padded with -1000, so any negative length ends a row's document list.
+    Numbering follows ``doc_ids_from_cu_seqlens``: the j-th document of a row
+    gets id j + 1.  Lengths summing past ``seq_len`` raise ``ValueError``.
+    """
+    lens = np.asarray(seq_lens).reshape(len(seq_lens), -1) if len(seq_lens) else np.zeros((0, 0))
+    out = np.full((lens.shape[0], seq_len), padding_value, dtype=np.int32)
+    for b in range(lens.shape[0]):
+        pos = 0
+        for j, n in enumerate(int(x) for x in lens[b]):
+            if n < 0:
+                break
+            if pos + n > seq_len:
+                raise ValueError("document lengths exceed seq_len")
+            for p in range(pos, pos + n):
+                out[b, p] = j + 1
+            pos += n
+    return out
+
+
+def segment_cu_seqlens(doc_ids_row) -> np.ndarray:
+    """Boundaries of maximal runs of equal ids covering the whole row.
+
+    glm5_next.cp page, ``segment_cu_seqlens``: "boundaries for consecutive
+    document-id runs covering the full row".  Padding runs are segments too,
+    equal ids in separate runs are separate segments.  Output int32
+    ``[R + 1]`` starting at 0 and ending at the row length (``[0]`` for an
+    empty row).
+    """
+    ids = [int(x) for x in np.asarray(doc_ids_row).reshape(-1)]
+    n = len(ids)
+    cu = [0]
+    for p in range(1, n):
+        if ids[p] != ids[p - 1]:
+            cu.append(p)
+    if n > 0:
+        cu.append(n)
+    return np.asarray(cu, dtype=np.int32)

@@ -1,0 +1,97 @@
+"""Pins for the boundary oracle (doc_ids_from_cu_seqlens, segment_cu_seqlens).
+
+Each check is fixed by something other than the oracle's own code: a worked
+example derived by hand, numpy brute force written a different way
+(``np.repeat`` / ``np.diff``), and round trips.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import PAD_DOC_ID
+
+
+def _runs_to_ids(spec):
+    ids = []
+    for tok in spec.split():
+        val, cnt = tok.split(":")
+        ids += [int(val)] * int(cnt)
+    return np.asarray(ids, dtype=np.int32)
+
+
+def test_worked_example(golden):
+    g = golden("boundary_cfg1.txt")
+    seq_len = int(g["seq_len"])
+    cu = np.asarray([int(x) for x in g["cu_seqlens"].split()], dtype=np.int32)
+    ids = oracle.doc_ids_from_cu_seqlens(cu, seq_len)
+    assert ids.shape == (1, seq_len) and ids.dtype == np.int32
+    np.testing.assert_array_equal(ids[0], _runs_to_ids(g["doc_ids_runs"]))
+    seg = oracle.segment_cu_seqlens(ids[0])
+    np.testing.assert_array_equal(seg, [int(x) for x in g["segments"].split()])
+
+
+def _brute_ids(cu, seq_len):
+    # ids by repetition: lead padding, one block per document, trailing padding
+    lens = np.diff(cu)
+    body = np.repeat(np.arange(1, len(lens) + 1, dtype=np.int64), lens)
+    return np.concatenate([np.full(cu[0], PAD_DOC_ID), body,
+                           np.full(seq_len - cu[-1], PAD_DOC_ID)]).astype(np.int32)
+
+
+def _brute_segments(ids):
+    if len(ids) == 0:
+        return np.zeros(1, dtype=np.int32)
+    starts = np.flatnonzero(np.diff(ids.astype(np.int64))) + 1
+    return np.concatenate([[0], starts, [len(ids)]]).astype(np.int32)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_against_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 12))
+    lens = rng.integers(0, 9, size=n)          # zero-length documents included
+    lead = int(rng.integers(0, 4))
+    tail = int(rng.integers(0, 5))
+    cu = np.concatenate([[lead], lead + np.cumsum(lens)]).astype(np.int32)
+    seq_len = int(cu[-1]) + tail
+    ids = oracle.doc_ids_from_cu_seqlens(cu, seq_len)[0]
+    np.testing.assert_array_equal(ids, _brute_ids(cu, seq_len))
+    np.testing.assert_array_equal(oracle.segment_cu_seqlens(ids), _brute_segments(ids))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_round_trip(seed):
+    rng = np.random.default_rng(100 + seed)
+    lens = rng.integers(1, 30, size=int(rng.integers(1, 10)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ids = oracle.doc_ids_from_cu_seqlens(cu, int(cu[-1]))
+    np.testing.assert_array_equal(oracle.segment_cu_seqlens(ids[0]), cu)
+
+
+def test_segments_split_repeated_ids_and_count_padding():
+    ids = np.asarray([5, 5, PAD_DOC_ID, PAD_DOC_ID, 5, 0, 0], dtype=np.int32)
+    np.testing.assert_array_equal(oracle.segment_cu_seqlens(ids), [0, 2, 4, 5, 7])
+
+
+def test_empty_and_degenerate():
+    np.testing.assert_array_equal(oracle.segment_cu_seqlens(np.zeros(0, np.int32)), [0])
+    assert oracle.doc_ids_from_cu_seqlens([0], 0).shape == (1, 0)
+    np.testing.assert_array_equal(oracle.doc_ids_from_cu_seqlens([0], 3)[0], [PAD_DOC_ID] * 3)
+    np.testing.assert_array_equal(oracle.doc_ids_from_cu_seqlens([0, 0, 2], 2)[0], [2, 2])
+    np.testing.assert_array_equal(oracle.segment_cu_seqlens([9]), [0, 1])
+
+
+@pytest.mark.parametrize("cu,seq_len", [([0, 5, 3], 6), ([0, 7], 6), ([-1, 2], 4), ([], 4)])
+def test_invalid_cu_raises(cu, seq_len):
+    with pytest.raises(ValueError):
+        oracle.doc_ids_from_cu_seqlens(np.asarray(cu, dtype=np.int64), seq_len)
+
+
+def test_seq_lens_variant_matches_cu_variant():
+    seq_lens = np.asarray([[3, 2, -1000], [1, 1, 4]])
+    ids = oracle.doc_ids_from_seq_lens(seq_lens, 7)
+    np.testing.assert_array_equal(ids[0], oracle.doc_ids_from_cu_seqlens([0, 3, 5], 7)[0])
+    np.testing.assert_array_equal(ids[1], oracle.doc_ids_from_cu_seqlens([0, 1, 2, 6], 7)[0])
+    with pytest.raises(ValueError):
+        oracle.doc_ids_from_seq_lens(np.asarray([[5, 5]]), 7)
