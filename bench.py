@@ -1,0 +1,165 @@
+"""Benchmark of the packed block-causal attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+
+One step = the whole device path over one batch of synthetic packed rows that
+is already resident in HBM:
+  doc_ids_from_cu_seqlens (per row) -> segment_cu_seqlens (per row)
+  -> tile schedule (plan) -> block-diagonal attention kernel.
+The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
+
+Default workload: the packed LLM row (B=1, S=L=8192, Hq=32, Hkv=8, D=128,
+uniform[128, 2048] document lengths, 107-token padding tail, seed 2).
+Prints ONE JSON line.  `roofline` describes the attention kernel alone, timed
+with HIP events on the stream it is launched on; `cpu_baseline` times the CPU
+fp64 oracle on the host cores over the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+METRIC = "useful TFLOP/s packed block-causal attention fwd; % of bf16 MFMA peak"
+ATTN_SOURCE = os.path.join(ROOT, "packed_sequence_block_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+
+
+def attn_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when they were taken on another kernel source or workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != attn_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(lay, q, k, v, budget_s: float = 10.0, max_passes: int = 4):
+    import torch
+    import oracle
+    ids = [oracle.doc_ids_from_cu_seqlens(lay.cu_seqlens(b), lay.S)[0] for b in range(lay.B)]
+    import numpy as np
+    ids = np.stack(ids)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.blockdiag_attn(q, k, v, ids, lay.seq_start, None, lay.enable_gqa)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= max_passes:
+            break
+    flops = lay.useful_flops() * passes
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"whole workload x{passes} (all {lay.B} rows, {lay.Hq} heads), {el:.1f} s, fp64 torch-CPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import packed_sequence_block_amd as psb
+    from packed_sequence_block_amd import _lib
+    from workloads import make_layout, make_qkv
+
+    lib = psb.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lay = make_layout(args.config)
+    q_cpu, k_cpu, v_cpu = make_qkv(lay)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
+    cus = [torch.as_tensor(lay.cu_seqlens(b)).to(dev) for b in range(B)]
+    doc_ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    seg_cu = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
+    seg_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws_bytes = psb.workspace_size(B, Hq, Hkv, L, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    scale = float(D) ** -0.5
+    gqa = 1 if lay.enable_gqa else 0
+    row_ptrs = [(P(cus[b]), cus[b].numel() - 1, ctypes.c_void_p(doc_ids[b].data_ptr()),
+                 ctypes.c_void_p(seg_cu[b].data_ptr()), ctypes.c_void_p(seg_n[b:].data_ptr()))
+                for b in range(B)]
+    qp, kp, vp, dp, op, wp = P(q), P(k), P(v), P(doc_ids), P(out), P(ws)
+
+    def step(ev0=None, ev1=None):
+        for cu_p, nd, ids_p, scu_p, sn_p in row_ptrs:
+            st = lib.psb_doc_ids_from_cu_seqlens(cu_p, nd, S, ids_p, None, sptr)
+            assert st == 0, st
+            st = lib.psb_segment_cu_seqlens(ids_p, S, scu_p, S + 1, sn_p, sptr)
+            assert st == 0, st
+        st = lib.psb_blockdiag_attn_plan(dp, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, wp, ws_bytes, sptr)
+        assert st == 0, st
+        if ev0 is not None:
+            ev0.record(stream)
+        st = lib.psb_blockdiag_attn_fwd_planned(qp, kp, vp, dp, B, Hq, Hkv, L, S, D, None, None, lay.seq_start,
+                                                scale, gqa, op, wp, ws_bytes, None, sptr)
+        assert st == 0, st
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    flops = lay.useful_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(lay.name)
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": lay.name, "B": B, "S": S, "L": L, "seq_start": lay.seq_start, "Hq": Hq,
+                   "Hkv": Hkv, "D": D, "documents": sum(len(r) for r in lay.doc_lens),
+                   "allowed_pairs": lay.allowed_pairs(), "useful_gflop_per_step": round(flops / 1e9, 3),
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(lay, q_cpu, k_cpu, v_cpu)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

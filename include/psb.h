@@ -1,0 +1,175 @@
+/*
+ * psb.h — packed-sequence block-diagonal attention for MI355X (gfx950).
+ *
+ * C ABI of the library libpsb.so.  Plain pointers and sizes only.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Device pointers point to memory the CALLER allocated (any HIP allocation on
+ *   the current device); the library never allocates, frees or keeps device
+ *   memory between calls.  Host pointers are read during the call only.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *   enqueues its kernels on that stream and returns without synchronizing; the
+ *   outputs are valid once the stream reaches that point.  Calls are reentrant.
+ * - The return value is a psb_status.  Argument errors are detected on the host
+ *   before anything is enqueued (nothing is launched, no device memory is
+ *   touched).  Errors that depend on device data are reported through the
+ *   optional device word `status_word` (bits OR-ed in by the kernels; the caller
+ *   zeroes it beforehand and reads it after synchronizing).
+ * - Document ids are int32.  The padding id is -1000 (PSB_PAD_DOC_ID).
+ *
+ * Sources: the "nemo_automodel.components.models.glm5_next.cp" page (API
+ * entries doc_ids_from_cu_seqlens and segment_cu_seqlens) and the
+ * "nemo_automodel.components.distributed.blockdiag_cp" page (package overview;
+ * cp_blockdiag_sdpa; BlockdiagCpModelState.packed_cu_seqlens).
+ */
+#ifndef PSB_H_
+#define PSB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t psb_status;
+
+#define PSB_OK 0
+#define PSB_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad scale, ... */
+#define PSB_ERR_SHAPE (-2)       /* inconsistent shapes / strides / shard range */
+#define PSB_ERR_UNSUPPORTED (-3) /* head dim other than 64 or 128 */
+#define PSB_ERR_CAPACITY (-4)    /* output or workspace buffer too small */
+#define PSB_ERR_HIP (-5)         /* a HIP runtime call failed (e.g. launch) */
+
+#define PSB_PAD_DOC_ID (-1000)
+
+/* Bits OR-ed into `status_word` by the kernels. */
+#define PSB_DATA_CU_NOT_MONOTONE 1   /* cu_seqlens decreases somewhere */
+#define PSB_DATA_CU_OUT_OF_RANGE 2   /* cu_seqlens[0] < 0 or cu_seqlens[N] > seq_len */
+#define PSB_DATA_DOC_NOT_CONTIGUOUS 4 /* a non-padding id occurs in two separate runs of a row */
+
+/* Human-readable message for a status code (static storage, never NULL). */
+const char* psb_status_string(psb_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t psb_version(void);
+
+/*
+ * Document ids from cumulative document boundaries (glm5_next.cp page,
+ * doc_ids_from_cu_seqlens: boundaries -> ids [1, sequence]).
+ *
+ *   cu_seqlens   device, int32 [n_docs + 1]: document i covers
+ *                positions [cu_seqlens[i], cu_seqlens[i+1]).
+ *   n_docs       number of documents (>= 0).
+ *   seq_len      row length S (>= 0).
+ *   doc_ids_out  device, int32 [seq_len]: one row of the [1, S] result.
+ *                Position p gets i + 1 for the document i covering it, and -1000
+ *                when no document covers it.
+ *   status_word  device int32 or NULL: PSB_DATA_CU_NOT_MONOTONE /
+ *                PSB_DATA_CU_OUT_OF_RANGE are OR-ed in when cu_seqlens is not
+ *                non-decreasing within [0, seq_len]; doc_ids_out is then
+ *                unspecified.
+ */
+psb_status psb_doc_ids_from_cu_seqlens(const int32_t* cu_seqlens, int64_t n_docs, int64_t seq_len,
+                                       int32_t* doc_ids_out, int32_t* status_word, void* stream);
+
+/*
+ * Boundaries of the maximal runs of equal document ids of one row, padding runs
+ * included (glm5_next.cp page, segment_cu_seqlens: run boundaries covering the
+ * full row).
+ *
+ *   doc_ids_row     device, int32 [seq_len].
+ *   cu_out          device, int32 [cu_capacity]; receives [0, run starts..., seq_len]
+ *                   (R + 1 entries for R runs; just [0] when seq_len == 0).
+ *   cu_capacity     must be >= seq_len + 1 (the worst case), else PSB_ERR_CAPACITY.
+ *   n_segments_out  device int32 scalar; receives R.
+ */
+psb_status psb_segment_cu_seqlens(const int32_t* doc_ids_row, int64_t seq_len, int32_t* cu_out,
+                                  int64_t cu_capacity, int32_t* n_segments_out, void* stream);
+
+/*
+ * Checks the precondition blockdiag_attn_fwd relies on: in every row of
+ * doc_ids [B, S] (row stride `row_stride` elements), each non-padding id forms
+ * one contiguous run (inkling2 context_parallel page, validate_document_positions:
+ * a gap never resumes an earlier document).  ORs PSB_DATA_DOC_NOT_CONTIGUOUS
+ * into status_word (required here) when violated.  Diagnostic, not on the hot path.
+ */
+psb_status psb_validate_doc_ids(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
+                                int32_t* status_word, void* stream);
+
+/* Bytes of device workspace psb_blockdiag_attn_fwd needs for this problem. */
+size_t psb_blockdiag_attn_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                             int64_t D);
+
+/*
+ * Block-diagonal (per-document causal) attention forward (blockdiag_cp page:
+ * package overview — a packed row needs a causal mask per document; and
+ * cp_blockdiag_sdpa — the local queries run against the delivered keys with a
+ * per-document causal mask rebuilt from the document ids; scale defaults to
+ * D**-0.5; enable_gqa as in PyTorch sdpa; output [B, Hq, L, D] for the local rows).
+ *
+ * The query at local row i of batch b is global position qpos = seq_start + i.
+ * It attends to key k iff doc_ids[b,k] == doc_ids[b,qpos], doc_ids[b,qpos] != -1000
+ * and k <= qpos.  A query with no allowed key (a padding query) outputs 0.
+ *
+ *   q            device bf16 [B, Hq, L, D]   (strides q_strides, elements; D contiguous)
+ *   k, v         device bf16 [B, Hkv, S, D]  (strides kv_strides, shared by k and v)
+ *   doc_ids      device int32 [B, S], contiguous.  Precondition: each non-padding
+ *                id forms one contiguous run per row (psb_validate_doc_ids checks it).
+ *   q_strides    host int64[3] = strides of (B, H, seq) in elements, or NULL for
+ *                contiguous [B, Hq, L, D]; kv_strides likewise for k and v.
+ *   seq_start    global position of local row 0; 0 <= seq_start, seq_start + L <= S.
+ *   scale        softmax scale (finite, > 0 not required); callers pass D**-0.5 for
+ *                the default.
+ *   enable_gqa   non-zero: query head h reads kv head h / (Hq / Hkv) (Hq % Hkv == 0).
+ *                Zero: requires Hq == Hkv, else PSB_ERR_SHAPE.
+ *   out          device bf16 [B, Hq, L, D], contiguous; must not alias q, k or v.
+ *   workspace    device, >= psb_blockdiag_attn_fwd_workspace_size(...) bytes,
+ *                16-byte aligned (scheduler tables; contents need no initialisation).
+ *   status_word  device int32 or NULL (unused by this call at present).
+ *
+ * D must be 64 or 128 (else PSB_ERR_UNSUPPORTED).  Empty problems (B, Hq, L == 0)
+ * enqueue nothing and return PSB_OK.
+ */
+psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v,
+                                  const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                  int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                  const int64_t* kv_strides, int64_t seq_start, float scale,
+                                  int32_t enable_gqa, void* out, void* workspace,
+                                  size_t workspace_bytes, int32_t* status_word, void* stream);
+
+/*
+ * The two halves of psb_blockdiag_attn_fwd, for callers that run many
+ * attention calls over one document layout (every layer of a model step shares
+ * doc_ids): plan once, then run per layer.  The package overview of the
+ * blockdiag_cp page lists "varlen metadata precompute" as the internal step this
+ * corresponds to.
+ *
+ * psb_blockdiag_attn_plan writes the tile schedule for (doc_ids, B, Hq, Hkv, L,
+ * S, seq_start, enable_gqa) into `workspace` (size from
+ * psb_blockdiag_attn_fwd_workspace_size).  D is checked only for support.
+ *
+ * psb_blockdiag_attn_fwd_planned launches the attention kernel alone; it reads
+ * the schedule from `workspace`, which must hold a plan made with the same
+ * doc_ids contents and the same shape arguments, enqueued earlier on the same
+ * stream (or otherwise ordered before this call).  A workspace that holds no such
+ * plan gives wrong outputs but no out-of-bounds access.  Arguments and errors are
+ * otherwise those of psb_blockdiag_attn_fwd.
+ */
+psb_status psb_blockdiag_attn_plan(const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                   int64_t S, int64_t D, int64_t seq_start, int32_t enable_gqa,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, const void* v,
+                                          const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                          int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                          const int64_t* kv_strides, int64_t seq_start, float scale,
+                                          int32_t enable_gqa, void* out, const void* workspace,
+                                          size_t workspace_bytes, int32_t* status_word, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSB_H_ */

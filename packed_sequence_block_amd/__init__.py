@@ -1,0 +1,16 @@
+"""Packed-sequence block-diagonal (per-document causal) attention for MI355X.
+
+Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
+
+* :func:`doc_ids_from_cu_seqlens` — document boundaries -> per-position ids
+* :func:`segment_cu_seqlens` — per-position ids -> run boundaries
+* :func:`blockdiag_attn_fwd` — attention with the per-document causal mask,
+  for a packed row (``seq_start = 0``, ``L = S``) or one context-parallel
+  rank's contiguous query shard against all delivered keys/values.
+"""
+
+from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_fwd, doc_ids_from_cu_seqlens, load,
+                   segment_cu_seqlens, status_string, validate_doc_ids, workspace_size)
+
+__all__ = ["PAD_DOC_ID", "PsbError", "blockdiag_attn_fwd", "doc_ids_from_cu_seqlens", "load",
+           "segment_cu_seqlens", "status_string", "validate_doc_ids", "workspace_size"]

@@ -1,0 +1,200 @@
+"""ctypes binding of libpsb.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; torch provides device
+memory and the current stream.  Loading fails loudly when the library has not
+been built: there is no other implementation behind these functions.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsb.so")
+
+PSB_OK = 0
+PSB_ERR_INVALID_ARG = -1
+PSB_ERR_SHAPE = -2
+PSB_ERR_UNSUPPORTED = -3
+PSB_ERR_CAPACITY = -4
+PSB_ERR_HIP = -5
+PAD_DOC_ID = -1000
+DATA_CU_NOT_MONOTONE = 1
+DATA_CU_OUT_OF_RANGE = 2
+DATA_DOC_NOT_CONTIGUOUS = 4
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/psb.h
+SIGNATURES = {
+    "psb_status_string": (ctypes.c_char_p, [_c_i32]),
+    "psb_version": (_c_i32, []),
+    "psb_doc_ids_from_cu_seqlens": (_c_i32, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "psb_segment_cu_seqlens": (_c_i32, [_vp, _c_i64, _vp, _c_i64, _vp, _vp]),
+    "psb_validate_doc_ids": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "psb_blockdiag_attn_fwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "psb_blockdiag_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, ctypes.c_size_t,
+                                        _vp, _vp]),
+    "psb_blockdiag_attn_plan": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32,
+                                         _vp, ctypes.c_size_t, _vp]),
+    "psb_blockdiag_attn_fwd_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                _c_i64, _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp,
+                                                ctypes.c_size_t, _vp, _vp]),
+}
+
+_lib = None
+
+
+class PsbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m packed_sequence_block_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().psb_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != PSB_OK:
+        raise PsbError(status, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("psb runs on the GPU only: pass device tensors")
+
+
+def doc_ids_from_cu_seqlens(cu_seqlens: torch.Tensor, seq_len: int,
+                            validate: bool = False) -> torch.Tensor:
+    """Document ids ``[1, seq_len]`` (int32) from boundaries ``[N + 1]``.
+
+    Document i gets id i + 1; uncovered positions get -1000.  With
+    ``validate=True`` the call synchronizes and raises ``ValueError`` when the
+    boundaries are not non-decreasing inside ``[0, seq_len]``.
+    """
+    _need_gpu(cu_seqlens)
+    cu = cu_seqlens.reshape(-1)
+    if cu.dtype != torch.int32:
+        cu = cu.to(torch.int32)
+    cu = cu.contiguous()
+    if cu.numel() < 1:
+        raise ValueError("cu_seqlens needs at least one entry")
+    out = torch.empty((1, int(seq_len)), dtype=torch.int32, device=cu.device)
+    status = torch.zeros(1, dtype=torch.int32, device=cu.device) if validate else None
+    _check(load().psb_doc_ids_from_cu_seqlens(_ptr(cu), cu.numel() - 1, int(seq_len), _ptr(out),
+                                              _ptr(status), _vp(_stream(cu))),
+           "doc_ids_from_cu_seqlens")
+    if validate and int(status.item()) != 0:
+        raise ValueError(f"cu_seqlens invalid (status bits {int(status.item())})")
+    return out
+
+
+def segment_cu_seqlens(doc_ids_row: torch.Tensor) -> torch.Tensor:
+    """Run boundaries ``[R + 1]`` (int32) of one row; synchronizes once to size the result."""
+    _need_gpu(doc_ids_row)
+    ids = doc_ids_row.reshape(-1)
+    if ids.dtype != torch.int32:
+        ids = ids.to(torch.int32)
+    ids = ids.contiguous()
+    S = ids.numel()
+    cu = torch.empty(S + 1, dtype=torch.int32, device=ids.device)
+    n = torch.empty(1, dtype=torch.int32, device=ids.device)
+    _check(load().psb_segment_cu_seqlens(_ptr(ids), S, _ptr(cu), S + 1, _ptr(n), _vp(_stream(ids))),
+           "segment_cu_seqlens")
+    return cu[: int(n.item()) + 1]
+
+
+def validate_doc_ids(doc_ids: torch.Tensor) -> None:
+    """Raises ``ValueError`` unless every non-padding id is one contiguous run per row."""
+    _need_gpu(doc_ids)
+    ids = doc_ids.reshape(doc_ids.shape[0] if doc_ids.dim() > 1 else 1, -1).to(torch.int32).contiguous()
+    status = torch.zeros(1, dtype=torch.int32, device=ids.device)
+    _check(load().psb_validate_doc_ids(_ptr(ids), ids.shape[0], ids.shape[1], ids.shape[1], _ptr(status),
+                                       _vp(_stream(ids))), "validate_doc_ids")
+    if int(status.item()) & DATA_DOC_NOT_CONTIGUOUS:
+        raise ValueError("a non-padding document id occurs in more than one run of a row")
+
+
+def workspace_size(B: int, Hq: int, Hkv: int, L: int, D: int) -> int:
+    return int(load().psb_blockdiag_attn_fwd_workspace_size(B, Hq, Hkv, L, D))
+
+
+def blockdiag_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_ids: torch.Tensor,
+                       seq_start: int = 0, scale: float | None = None, enable_gqa: bool = False,
+                       out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       validate: bool = False) -> torch.Tensor:
+    """Block-diagonal causal attention forward: ``out [B, Hq, L, D]`` (bf16).
+
+    ``q [B, Hq, L, D]`` and ``k, v [B, Hkv, S, D]`` are bf16 with the last dim
+    contiguous; ``doc_ids [B, S]`` int32 (global positions, -1000 = padding).
+    ``scale=None`` means ``D ** -0.5``.  ``workspace`` (uint8, at least
+    :func:`workspace_size` bytes) may be passed to avoid an allocation per call.
+    """
+    _need_gpu(q, k, v, doc_ids)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D bfloat16 tensor")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    B, Hq, L, D = q.shape
+    S = k.shape[2]
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shape does not match q")
+    ids = doc_ids.reshape(B, -1) if doc_ids.dim() != 2 else doc_ids
+    if ids.dtype != torch.int32:
+        ids = ids.to(torch.int32)
+    ids = ids.contiguous()
+    if tuple(ids.shape) != (B, S):
+        raise ValueError(f"doc_ids must be [B, S] = [{B}, {S}]")
+    if validate:
+        validate_doc_ids(ids)
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    elif out.shape != (B, Hq, L, D) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B, Hq, L, D] tensor")
+    need = workspace_size(B, Hq, Hkv, L, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    qs = (ctypes.c_int64 * 3)(*q.stride()[:3])
+    kvs = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    status = load().psb_blockdiag_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(ids), B, Hq, Hkv, L, S, D, qs, kvs, int(seq_start), sc,
+        1 if enable_gqa else 0, _ptr(out), _ptr(workspace), need, None, _vp(_stream(q)))
+    _check(status, "blockdiag_attn_fwd")
+    return out

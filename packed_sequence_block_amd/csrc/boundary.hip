@@ -1,0 +1,181 @@
+// Document-id and segment-boundary kernels.
+//
+// glm5_next.cp page, API entries doc_ids_from_cu_seqlens (cumulative document
+// boundaries -> ids [1, sequence]) and segment_cu_seqlens (boundaries of the
+// runs of equal ids that cover the whole row).  Both are O(S) integer passes
+// bound by launch latency at the sizes packed training uses (S <= 64K): the
+// designs below aim at few launches and coalesced int4 traffic, not at FLOPs.
+#include "psb_internal.h"
+
+namespace psb {
+namespace {
+
+// ---- doc_ids_from_cu_seqlens ---------------------------------------------------
+// One thread per position: the position's document is the last boundary
+// cu[i] <= p (binary search over the n_docs + 1 boundaries), provided p < cu[n_docs].
+// Threads below n_docs also check that the boundaries are non-decreasing.
+__global__ void __launch_bounds__(256) doc_ids_kernel(const int32_t* __restrict__ cu, int32_t n_docs,
+                                                      int32_t seq_len, int32_t* __restrict__ ids,
+                                                      int32_t* __restrict__ status) {
+  const int32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (status != nullptr) {
+    int32_t bits = 0;
+    if (p < n_docs && cu[p + 1] < cu[p]) bits |= PSB_DATA_CU_NOT_MONOTONE;
+    if (p == 0 && (cu[0] < 0 || cu[n_docs] > seq_len)) bits |= PSB_DATA_CU_OUT_OF_RANGE;
+    if (bits) atomicOr(status, bits);
+  }
+  if (p >= seq_len) return;
+  // largest i in [0, n_docs] with cu[i] <= p, or -1
+  int32_t lo = 0, hi = n_docs + 1;  // search in [lo, hi)
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (cu[mid] <= p) lo = mid + 1; else hi = mid;
+  }
+  const int32_t i = lo - 1;
+  ids[p] = (i >= 0 && i < n_docs) ? i + 1 : PSB_PAD_DOC_ID;
+}
+
+// ---- segment_cu_seqlens -----------------------------------------------------------
+// A single workgroup walks the row in chunks of kSegThreads * kSegItems positions.
+// Each thread flags the run starts among its kSegItems consecutive positions,
+// a workgroup-wide exclusive scan of the per-thread counts gives each thread its
+// output slot, and the running total carries across chunks.
+constexpr int kSegThreads = 1024;
+constexpr int kSegItems = 16;
+
+__global__ void __launch_bounds__(kSegThreads) segment_kernel(const int32_t* __restrict__ ids,
+                                                              int32_t seq_len,
+                                                              int32_t* __restrict__ cu_out,
+                                                              int32_t* __restrict__ n_out) {
+  __shared__ int32_t wave_tot[kSegThreads / kWave];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid % kWave, wid = tid / kWave;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < seq_len; base += (int64_t)kSegThreads * kSegItems) {
+    const int64_t p0 = base + (int64_t)tid * kSegItems;
+    int32_t v[kSegItems];
+    if (p0 + kSegItems <= seq_len && (reinterpret_cast<uintptr_t>(ids + p0) % 16) == 0) {
+      const int4* src = reinterpret_cast<const int4*>(ids + p0);
+#pragma unroll
+      for (int j = 0; j < kSegItems / 4; ++j) {
+        const int4 t = src[j];
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSegItems; ++j) v[j] = (p0 + j < seq_len) ? ids[p0 + j] : 0;
+    }
+    const int32_t prev = (p0 > 0 && p0 < seq_len) ? ids[p0 - 1] : 0;
+    uint32_t flags = 0;
+#pragma unroll
+    for (int j = 0; j < kSegItems; ++j) {
+      const int64_t p = p0 + j;
+      const int32_t before = (j == 0) ? prev : v[j - 1];
+      if (p > 0 && p < seq_len && v[j] != before) flags |= 1u << j;
+    }
+    const int32_t cnt = __popc(flags);
+    // inclusive scan of cnt across the wave
+    int32_t inc = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t t = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += t;
+    }
+    if (lane == kWave - 1) wave_tot[wid] = inc;
+    __syncthreads();
+    int32_t wave_off = 0, chunk_tot = 0;
+    for (int w = 0; w < kSegThreads / kWave; ++w) {
+      const int32_t t = wave_tot[w];
+      wave_off += (w < wid) ? t : 0;
+      chunk_tot += t;
+    }
+    int32_t slot = carry + wave_off + inc - cnt + 1;  // +1: cu_out[0] is the leading 0
+    while (flags) {
+      const int j = __ffs(flags) - 1;
+      flags &= flags - 1;
+      cu_out[slot++] = (int32_t)(p0 + j);
+    }
+    __syncthreads();  // everyone has read carry and wave_tot
+    if (tid == 0) carry += chunk_tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    cu_out[0] = 0;
+    if (seq_len > 0) {
+      cu_out[carry + 1] = seq_len;
+      *n_out = carry + 1;
+    } else {
+      *n_out = 0;
+    }
+  }
+}
+
+// ---- contiguity check ------------------------------------------------------------
+// One wave per (row, position).  A wave whose position starts a non-padding run
+// scans every earlier position of the row for the same id; finding one means the
+// id occurs in two separate runs.  Cost is (number of runs) x S / 64 wave steps.
+__global__ void __launch_bounds__(256) contiguity_kernel(const int32_t* __restrict__ ids, int64_t B,
+                                                         int32_t S, int64_t row_stride,
+                                                         int32_t* __restrict__ status) {
+  const int64_t wave_global = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (wave_global >= B * S) return;  // tail waves of the last workgroup
+  const int64_t b = wave_global / S;
+  const int32_t p = (int32_t)(wave_global % S);
+  const int32_t* row = ids + b * row_stride;
+  const int32_t x = row[p];
+  if (x == PSB_PAD_DOC_ID || (p > 0 && row[p - 1] == x)) return;
+  bool dup = false;
+  for (int32_t base = 0; base < p; base += kWave) {
+    const int32_t j = base + lane;
+    if (j < p && row[j] == x) dup = true;
+  }
+  if (__any(dup) && lane == 0) atomicOr(status, PSB_DATA_DOC_NOT_CONTIGUOUS);
+}
+
+}  // namespace
+}  // namespace psb
+
+using namespace psb;
+
+PSB_API psb_status psb_doc_ids_from_cu_seqlens(const int32_t* cu_seqlens, int64_t n_docs, int64_t seq_len,
+                                               int32_t* doc_ids_out, int32_t* status_word, void* stream) {
+  if (cu_seqlens == nullptr || n_docs < 0 || seq_len < 0) return PSB_ERR_INVALID_ARG;
+  if (seq_len > 0 && doc_ids_out == nullptr) return PSB_ERR_INVALID_ARG;
+  if (n_docs >= INT32_MAX || seq_len >= INT32_MAX) return PSB_ERR_SHAPE;
+  const int64_t work = seq_len > n_docs + 1 ? seq_len : n_docs + 1;
+  const int threads = 256;
+  const int64_t blocks = ceil_div(work, threads);
+  doc_ids_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, as_stream(stream)>>>(
+      cu_seqlens, (int32_t)n_docs, (int32_t)seq_len, doc_ids_out, status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_segment_cu_seqlens(const int32_t* doc_ids_row, int64_t seq_len, int32_t* cu_out,
+                                          int64_t cu_capacity, int32_t* n_segments_out, void* stream) {
+  if (seq_len < 0 || cu_out == nullptr || n_segments_out == nullptr) return PSB_ERR_INVALID_ARG;
+  if (seq_len > 0 && doc_ids_row == nullptr) return PSB_ERR_INVALID_ARG;
+  if (seq_len >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (cu_capacity < seq_len + 1) return PSB_ERR_CAPACITY;
+  segment_kernel<<<dim3(1), dim3(kSegThreads), 0, as_stream(stream)>>>(doc_ids_row, (int32_t)seq_len,
+                                                                         cu_out, n_segments_out);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_validate_doc_ids(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
+                                        int32_t* status_word, void* stream) {
+  if (B < 0 || S < 0 || status_word == nullptr) return PSB_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return PSB_OK;
+  if (doc_ids == nullptr) return PSB_ERR_INVALID_ARG;
+  if (row_stride < S || S >= INT32_MAX) return PSB_ERR_SHAPE;
+  const int64_t waves = B * S;
+  const int64_t blocks = ceil_div(waves, 256 / kWave);
+  if (blocks >= INT32_MAX) return PSB_ERR_SHAPE;
+  contiguity_kernel<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(doc_ids, B, (int32_t)S,
+                                                                                  row_stride, status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}

@@ -1,0 +1,143 @@
+// Tile scheduler for block-diagonal attention: which keys each query block needs.
+//
+// The mask (blockdiag_cp page, package overview and cp_blockdiag_sdpa) lets the
+// query at global position q see keys [start(q), q] where start(q) is the first
+// position of q's document — given that each non-padding id is one contiguous
+// run of its row.  For a block of 32 consecutive query rows the union of those
+// ranges is [start(first valid row), last valid row + 1): every key tile in that
+// range holds at least one allowed pair unless the block straddles documents.
+//
+// Kernel 1 (one wave per 32-row block) computes that range.  The document start
+// is found by a 64-way search: "doc[p] == doc[q]" is false before start(q) and
+// true from there to q, so each step probes 64 positions and keeps the bracket
+// around the first true one (3 dependent steps for S = 64K).
+// Kernel 2 (one workgroup) merges NR blocks into a row tile, and orders the tiles
+// by descending key-range length (counting sort), so the attention grid starts
+// the longest tiles first.
+#include "psb_internal.h"
+#include "schedule.h"
+
+namespace psb {
+namespace {
+
+__global__ void __launch_bounds__(256) block_range_kernel(const int32_t* __restrict__ doc_ids, int32_t S,
+                                                          int32_t L, int32_t seq_start, int32_t nblk,
+                                                          int32_t total_blocks, int32_t* __restrict__ blk_lo,
+                                                          int32_t* __restrict__ blk_hi) {
+  const int32_t wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (wid >= total_blocks) return;
+  const int32_t b = wid / nblk, blk = wid % nblk;
+  const int32_t* row = doc_ids + (int64_t)b * S;
+  const int32_t r = blk * kRowsPerBlock + (lane % kRowsPerBlock);
+  const bool valid = lane < kRowsPerBlock && r < L && row[seq_start + r] != PSB_PAD_DOC_ID;
+  const uint64_t m = __ballot(valid);
+  if (m == 0) {
+    if (lane == 0) { blk_lo[wid] = 0; blk_hi[wid] = 0; }
+    return;
+  }
+  const int32_t first = __ffsll((unsigned long long)m) - 1;
+  const int32_t last = 63 - __clzll((long long)m);
+  const int32_t qf = seq_start + blk * kRowsPerBlock + first;
+  const int32_t x = row[qf];
+  int32_t lo = 0, hi = qf;  // the document start lies in [lo, hi]; doc[hi] == x
+  while (lo < hi) {
+    const int32_t step = (hi - lo + kWave - 1) / kWave;
+    int32_t p = lo + lane * step;
+    if (p > hi) p = hi;
+    const uint64_t t = __ballot(row[p] == x);
+    if (t == 0) {
+      // every probe lies before the start: it is beyond lane 63's probe
+      lo = lo + (kWave - 1) * step + 1;
+    } else {
+      const int32_t i = __ffsll((unsigned long long)t) - 1;
+      const int32_t pi = min(hi, lo + i * step);
+      lo = (i == 0) ? lo : lo + (i - 1) * step + 1;
+      hi = pi;
+    }
+  }
+  if (lane == 0) {
+    blk_lo[wid] = lo;
+    blk_hi[wid] = seq_start + blk * kRowsPerBlock + last + 1;
+  }
+}
+
+constexpr int kSortThreads = 1024;
+constexpr int kBuckets = 2048;
+
+__device__ inline int32_t tile_iters(int32_t lo, int32_t hi) {
+  return hi > lo ? (hi - lo + kKeysPerTile - 1) / kKeysPerTile : 0;
+}
+
+__global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t* __restrict__ blk_lo,
+                                                                  const int32_t* __restrict__ blk_hi,
+                                                                  int32_t B, int32_t nblk, int32_t nr,
+                                                                  int32_t ntile_row,
+                                                                  int32_t* __restrict__ tile_lo,
+                                                                  int32_t* __restrict__ tile_hi,
+                                                                  int32_t* __restrict__ order) {
+  __shared__ int32_t hist[kBuckets];
+  __shared__ int32_t wsum[kSortThreads / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int32_t T = B * ntile_row;
+  for (int i = tid; i < kBuckets; i += kSortThreads) hist[i] = 0;
+  __syncthreads();
+  for (int32_t t = tid; t < T; t += kSortThreads) {
+    const int32_t b = t / ntile_row, rt = t % ntile_row;
+    int32_t lo = 0x7fffffff, hi = 0;
+    for (int32_t j = 0; j < nr; ++j) {
+      const int32_t blk = rt * nr + j;
+      if (blk >= nblk) break;
+      const int32_t l = blk_lo[b * nblk + blk], h = blk_hi[b * nblk + blk];
+      if (h > l) { lo = min(lo, l); hi = max(hi, h); }
+    }
+    if (hi == 0) lo = 0;
+    tile_lo[t] = lo;
+    tile_hi[t] = hi;
+    atomicAdd(&hist[min(tile_iters(lo, hi), kBuckets - 1)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in DESCENDING bucket order: offset(bk) = sum of hist[bk' > bk].
+  // Thread tid owns reversed buckets 2*tid and 2*tid+1.
+  const int r0 = 2 * tid, r1 = 2 * tid + 1;
+  const int32_t c0 = hist[kBuckets - 1 - r0], c1 = hist[kBuckets - 1 - r1];
+  int32_t inc = c0 + c1;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t v = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += v;
+  }
+  if (lane == kWave - 1) wsum[wv] = inc;
+  __syncthreads();
+  int32_t base = 0;
+  for (int w = 0; w < wv; ++w) base += wsum[w];
+  const int32_t excl = base + inc - c0 - c1;
+  __syncthreads();  // all reads of hist done before it is overwritten with offsets
+  hist[kBuckets - 1 - r0] = excl;
+  hist[kBuckets - 1 - r1] = excl + c0;
+  __syncthreads();
+  for (int32_t t = tid; t < T; t += kSortThreads) {
+    const int32_t bk = min(tile_iters(tile_lo[t], tile_hi[t]), kBuckets - 1);
+    order[atomicAdd(&hist[bk], 1)] = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
+                           int32_t nr, const ScheduleBuffers& buf, hipStream_t stream) {
+  const int32_t nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int32_t total = B * nblk;
+  const int waves_per_wg = 256 / kWave;
+  const int32_t grid = (total + waves_per_wg - 1) / waves_per_wg;
+  block_range_kernel<<<dim3(grid), dim3(256), 0, stream>>>(doc_ids, S, L, seq_start, nblk, total, buf.blk_lo,
+                                                           buf.blk_hi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int32_t ntile_row = (nblk + nr - 1) / nr;
+  tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
+                                                                buf.tile_lo, buf.tile_hi, buf.order);
+  return hipGetLastError();
+}
+
+}  // namespace psb

@@ -1,0 +1,116 @@
+"""Full-size named workloads on the GPU, in the launch configuration the benchmark times.
+
+The oracle cannot produce whole outputs at these sizes in seconds, so each
+config is checked three ways: sampled rows (all heads) against the oracle row by
+row; the closed form for q = 0 (each row is the plain mean of V over its
+document prefix, computed here with an fp64 cumulative sum); and, for the
+context-parallel shard, equality with the same rows of the unsharded problem.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import MAX_ABS, MEAN_ABS, compare, oracle_doc_ids, say
+from workloads import make_layout, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def psb():
+    import packed_sequence_block_amd as m
+    m.load()
+    return m
+
+
+def sample_rows(lay, ids_row, rng, n=48):
+    """Local rows to check: document starts/ends, shard edges, padding, random."""
+    lo, hi = lay.seq_start, lay.seq_start + lay.L
+    cu = oracle.segment_cu_seqlens(ids_row)
+    picks = {0, lay.L - 1, min(lay.L - 1, 31), min(lay.L - 1, 32)}
+    for p in cu:
+        for d in (-1, 0, 1, 63, 64):
+            if lo <= p + d < hi:
+                picks.add(int(p + d - lo))
+    picks = sorted(picks)
+    if len(picks) > n // 2:
+        picks = sorted(rng.choice(picks, n // 2, replace=False).tolist())
+    extra = rng.integers(0, lay.L, size=n - len(picks))
+    return sorted(set(picks) | set(int(x) for x in extra))
+
+
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_sampled_rows(psb, c):
+    lay = make_layout(c)
+    q, k, v = make_qkv(lay)
+    ids = oracle_doc_ids(lay)
+    say("config", c, lay.name, "sampled rows")
+    out = psb.blockdiag_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(ids).cuda(), lay.seq_start,
+                                 None, True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(c)
+    errs = []
+    for b in range(lay.B):
+        rows = sample_rows(lay, ids[b], rng, n=48 if lay.B == 1 else 16)
+        ref = oracle.blockdiag_attn_rows(q, k, v, ids, lay.seq_start, None, True, b, rows)  # [n, Hq, D]
+        got = out[b, :, rows].permute(1, 0, 2).cpu()
+        pad = torch.as_tensor(ids[b, lay.seq_start + np.asarray(rows)] == oracle.PAD_DOC_ID)
+        errs.append(compare(got, ref, pad, f"cfg{c} row{b}"))
+    say("config", c, "max/mean abs err", max(e[0] for e in errs), max(e[1] for e in errs))
+
+
+def prefix_mean_reference(v, ids_t, seq_start, L):
+    """Mean of V over [doc start, q] for every local row (0 for padding rows), fp64."""
+    B, H, S, D = v.shape
+    vd = v.double()
+    cs = torch.cumsum(vd, dim=2)
+    cs = torch.cat([torch.zeros_like(cs[:, :, :1]), cs], dim=2)          # cs[j] = sum of v[:j]
+    pos = torch.arange(S, device=v.device)
+    flag = torch.ones((B, S), dtype=torch.bool, device=v.device)
+    flag[:, 1:] = ids_t[:, 1:] != ids_t[:, :-1]
+    start = torch.cummax(torch.where(flag, pos, torch.zeros_like(pos)), dim=1).values   # run start [B, S]
+    qpos = torch.arange(seq_start, seq_start + L, device=v.device)
+    st = start[:, qpos]                                                   # [B, L]
+    cnt = (qpos.unsqueeze(0) - st + 1).double()
+    hi = cs[:, :, qpos + 1]                                               # [B, H, L, D]
+    lo = torch.gather(cs, 2, st.unsqueeze(1).unsqueeze(-1).expand(B, H, L, D))
+    mean = (hi - lo) / cnt.unsqueeze(1).unsqueeze(-1)
+    pad = (ids_t[:, qpos] == oracle.PAD_DOC_ID)
+    return torch.where(pad.unsqueeze(1).unsqueeze(-1), torch.zeros_like(mean), mean), pad
+
+
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_zero_query_closed_form(psb, c):
+    lay = make_layout(c)
+    _, k, v = make_qkv(lay)
+    ids_t = torch.as_tensor(oracle_doc_ids(lay)).cuda()
+    q = torch.zeros(lay.shapes()[0], dtype=torch.bfloat16, device="cuda")
+    kd, vd = k.cuda(), v.cuda()
+    say("config", c, "q = 0 closed form")
+    out = psb.blockdiag_attn_fwd(q, kd, vd, ids_t, lay.seq_start, None, True)
+    torch.cuda.synchronize()
+    r = lay.Hq // lay.Hkv
+    ref, pad = prefix_mean_reference(vd, ids_t, lay.seq_start, lay.L)
+    ref = ref.repeat_interleave(r, dim=1)
+    diff = (out.double() - ref).abs()
+    assert torch.isfinite(out.double()).all()
+    assert diff.max().item() <= MAX_ABS and diff.mean().item() <= MEAN_ABS, (diff.max().item(), diff.mean().item())
+    assert torch.all(out[pad.unsqueeze(1).expand(lay.B, lay.Hq, lay.L)] == 0)
+
+
+def test_cp_shard_matches_unsharded_rows(psb):
+    lay = make_layout(3)
+    q_shard, k, v = make_qkv(lay)
+    ids_t = torch.as_tensor(oracle_doc_ids(lay)).cuda()
+    kd, vd = k.cuda(), v.cuda()
+    # the full-row problem whose rows [seq_start, seq_start + L) are the shard's queries
+    g = torch.Generator().manual_seed(4242)
+    q_full = torch.randn((1, lay.Hq, lay.S, lay.D), generator=g).to(torch.bfloat16)
+    q_full[:, :, lay.seq_start:lay.seq_start + lay.L] = q_shard
+    say("config 3 shard vs unsharded")
+    full = psb.blockdiag_attn_fwd(q_full.cuda(), kd, vd, ids_t, 0, None, True)
+    part = psb.blockdiag_attn_fwd(q_shard.cuda(), kd, vd, ids_t, lay.seq_start, None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full[:, :, lay.seq_start:lay.seq_start + lay.L])
