@@ -28,6 +28,7 @@
 // mask; the rest compare each key with the row's [doc start, row] range.
 #include <math.h>
 
+
 #include "psb_internal.h"
 #include "schedule.h"
 
@@ -39,6 +40,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
@@ -55,11 +58,8 @@ struct AttnParams {
   int32_t B, Hq, Hkv, L, S, seq_start, group;
   int32_t nblk, ntile_row, units;
   float sc;  // softmax scale * log2(e)
-  const int32_t* blk_lo;
-  const int32_t* blk_hi;
-  const int32_t* tile_lo;
-  const int32_t* tile_hi;
-  const int32_t* order;
+  int64_t items;  // row tiles x head units
+  const TileRecord* work;
 };
 
 // XOR swizzle of the 16-byte chunks of an LDS row (row = D bf16).  D = 128: the
@@ -80,38 +80,70 @@ __device__ __forceinline__ int lds_index(int row, int col) {  // col in bf16 ele
   return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
 }
 
-__device__ __forceinline__ short4v tr_read(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4v*)(p));
+__device__ __forceinline__ short4v tr_read(const __bf16* ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(ptr));
 }
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2 cvt_bf16x2(float a, float b) {
+  const float2v f = {a, b};
+  return __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+}
+
+__device__ __forceinline__ float partner_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float partner_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// dword 3 of a raw buffer resource for gfx9-class GPUs (32-bit data format, no
+// swizzle); loads at offsets >= num_records return 0
+constexpr int kBufferFlags = 0x00020000;
+// the running row max is only moved (and O, l rescaled) when a tile's max exceeds
+// it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int NH>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int NR = kWaves / NH;
-  constexpr int NCH = D / 8;                               // 16-byte chunks per row
-  constexpr int KS = D / 16;                               // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;                               // 32-row blocks of O^T
-  constexpr int CPT = kKeysPerTile * NCH / kThreads;       // chunks per thread per tensor
-  static_assert(CPT * kThreads == kKeysPerTile * NCH, "tile must split evenly");
+  constexpr int KS = D / 16;                              // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;                              // 32-row blocks of O^T
+  constexpr int NCH = D / 8;                              // 16-byte chunks per row
+  constexpr int TILE_ELEMS = kKeysPerTile * D;            // one tensor, one stage
+  constexpr int CPT = TILE_ELEMS / 8 / kThreads;          // 16-byte chunks per thread per tensor
+  static_assert(CPT * kThreads * 8 == TILE_ELEMS, "tile must split evenly");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kKeysPerTile * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kKeysPerTile * D];
+  // [stage][K, V][64 keys x D], rows XOR-swizzled in 16-byte chunks
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[2][2][TILE_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = lane >> 5, lr = lane & 31;
-  const int32_t rank = blockIdx.x / p.units, unit = blockIdx.x % p.units;
-  const int32_t tile = p.order[rank];
-  // the tables come from the caller's workspace: never index with an entry that a
+  const int64_t row_bytes = p.kv_ss * 2;
+  const bool neg = p.sc < 0.f;
+  const float sc = neg ? -p.sc : p.sc;
+  const floatx16 zero16 = {};
+  const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
+
+  // workgroup blockIdx.x takes items blockIdx.x, + gridDim.x, ... (one item when the
+  // grid covers them all); with 8 kv heads, unit % Hkv == blockIdx.x % 8 keeps each
+  // kv head on one XCD
+  for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
+  const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
+  const TileRecord& rec = p.work[rank];
+  const int32_t b = rec.b, rt = rec.rt;
+  // the records come from the caller's workspace: never index with a value that a
   // plan for this shape cannot have written
-  if (tile < 0 || tile >= p.B * p.ntile_row) return;
-  const int32_t b = tile / p.ntile_row, rt = tile % p.ntile_row;
+  if (b < 0 || b >= p.B || rt < 0 || rt >= p.ntile_row) continue;
   const int32_t g = unit % p.Hkv, sub = unit / p.Hkv;
   const int32_t hq = g * p.group + sub * NH + (wv % NH);
   const int32_t blk = rt * NR + wv / NH;
   const int32_t row_local = blk * kRowsPerBlock + lr;
   const bool row_in = blk < p.nblk && row_local < p.L;
   const int32_t qpos = p.seq_start + row_local;
-  const int32_t tlo = max(p.tile_lo[tile], 0), thi = min(p.tile_hi[tile], p.S);
+  const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
   __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
 
   if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0
@@ -122,17 +154,50 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = z;
     }
-    return;
+    continue;
   }
 
-  // ---- per-wave query block description ------------------------------------------
-  int32_t w_lo = 0, w_hi = 0;
-  if (blk < p.nblk) {
-    w_lo = p.blk_lo[(int64_t)b * p.nblk + blk];
-    w_hi = p.blk_hi[(int64_t)b * p.nblk + blk];
+  // ---- K/V tile loads: buffer loads (zero past the key range) -> VGPRs -> LDS --------
+  // Staged through registers rather than LDS-direct loads: the transpose reads of V
+  // carry no alias information, so any LDS-writing load still in flight would make
+  // the compiler wait for it before every one of them.
+  const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
+  const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
+  int32_t goff[CPT];   // byte offset of this thread's chunk j within a tile (global)
+  int32_t loff[CPT];   // element offset of the same chunk in an LDS tile (swizzled)
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int ci = tid + j * kThreads;
+    const int row = ci / NCH, c = ci % NCH;
+    goff[j] = (int32_t)(row * row_bytes) + 16 * c;
+    loff[j] = lds_index<D>(row, 8 * c);
   }
-  w_lo = __builtin_amdgcn_readfirstlane(w_lo);
-  w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+  u32x4 kr[CPT], vr[CPT];
+  auto gload = [&](int32_t kt) {
+    const int32_t nrows = min(thi - kt, kKeysPerTile);
+    const int32_t nbytes = (int32_t)(nrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kt * p.kv_ss), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kt * p.kv_ss), (short)0, nbytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      kr[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, goff[j], 0, 0);
+      vr[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, goff[j], 0, 0);
+    }
+  };
+  auto lstore = [&](int stage) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      *(u32x4*)(&smem[stage][0][loff[j]]) = kr[j];
+      *(u32x4*)(&smem[stage][1][loff[j]]) = vr[j];
+    }
+  };
+  gload(tlo);
+
+  // ---- per-wave query block description ------------------------------------------
+  const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
+  const int32_t w_hi = __builtin_amdgcn_readfirstlane(rec.blk_hi[wv / NH]);
   const int32_t* docrow = p.doc + (int64_t)b * p.S;
   const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
   const bool valid = dq != PSB_PAD_DOC_ID;
@@ -140,13 +205,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   const bool flag = (lr == 0) || (dq != dprev);
   const uint64_t fm = __ballot(flag) & 0xffffffffull;
   const uint64_t upto = fm & ((2ull << lr) - 1ull);
-  const int rs = 63 - __clzll((long long)upto);            // last run start at or before my row
-  const int32_t wq0 = p.seq_start + blk * kRowsPerBlock;    // global position of the block's row 0
-  const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;      // my document's first position
-  const int32_t qlim = valid ? qpos : -1;                   // last allowed key (none for padding)
-  const bool single = (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull);
+  const int rs = 63 - __clzll((long long)upto);             // last run start at or before my row
+  const int32_t wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
+  const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;       // my document's first position
+  // key k is allowed iff 0 <= k - start_q <= span (unsigned compare); padding rows: none
+  const uint32_t span = valid ? (uint32_t)(qpos - start_q) : 0u;
+  const int32_t kshift = valid ? start_q : 0x40000000;       // padding: k - kshift < 0 always
+  const bool single = __builtin_amdgcn_readfirstlane(
+      (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
 
-  // ---- Q^T operand, resident for the whole tile loop -------------------------------
+  // ---- Q^T operand, resident for the whole tile loop (sign-flipped if scale < 0) -------
   bf16x8 qreg[KS];
   {
     const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
@@ -158,37 +226,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) qreg[ks][t] = (__bf16)0.f;
       }
-    }
-  }
-
-  const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
-  const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
-  bf16x8 kr[CPT], vr[CPT];
-  auto gload = [&](int32_t kt) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ci = tid + j * kThreads;
-      const int row = ci / NCH, c = ci % NCH;
-      const int32_t kg = kt + row;
-      if (kg < thi) {
-        kr[j] = *(const bf16x8*)(kbase + (int64_t)kg * p.kv_ss + 8 * c);
-        vr[j] = *(const bf16x8*)(vbase + (int64_t)kg * p.kv_ss + 8 * c);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) { kr[j][t] = (__bf16)0.f; vr[j][t] = (__bf16)0.f; }
+      if (neg) {
+        short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
+        bits ^= (short)0x8000;
+        qreg[ks] = __builtin_bit_cast(bf16x8, bits);
       }
     }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ci = tid + j * kThreads;
-      const int row = ci / NCH, c = ci % NCH;
-      const int idx = lds_index<D>(row, 8 * c);
-      *(bf16x8*)(sK + idx) = kr[j];
-      *(bf16x8*)(sV + idx) = vr[j];
-    }
-  };
+  }
 
   floatx16 o[DB];
 #pragma unroll
@@ -197,93 +241,106 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(tlo);
-  for (int32_t kt = tlo; kt < thi; kt += kKeysPerTile) {
-    __syncthreads();  // previous tile fully consumed
-    lstore();
-    __syncthreads();
-    if (kt + kKeysPerTile < thi) gload(kt + kKeysPerTile);
+  __syncthreads();  // the previous item's last tile is no longer read from LDS
+  lstore(0);        // waits for the first tile's loads
 
-    float sv[2][16];
-    bool act[2];
+  int stage = 0;
+  for (int32_t kt = tlo; kt < thi; kt += kKeysPerTile, stage ^= 1) {
+    __syncthreads();  // `stage` written by everyone; stage^1 no longer read
+    const bool more = kt + kKeysPerTile < thi;
+    if (more) gload(kt + kKeysPerTile);
+    const __bf16* sK = smem[stage][0];
+    const __bf16* sV = smem[stage][1];
+
+    const bool a0 = (kt < w_hi) && (kt + 32 > w_lo);
+    const bool a1 = (kt + 32 < w_hi) && (kt + 64 > w_lo);
+    if (a0 || a1) {
+      // ---- S^T = K Q^T per active 32-key block; K operand reads issued first -----------
+      floatx16 sv[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int32_t k0 = kt + 32 * kb;
-      act[kb] = (k0 < w_hi) && (k0 + 32 > w_lo);
-      if (act[kb]) {
-        floatx16 acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 0 ? !a0 : !a1) continue;
+        const int32_t k0 = kt + 32 * kb;
         const int krow = 32 * kb + lr;
+        bf16x8 ka[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(sK + lds_index<D>(krow, 16 * ks + 8 * h));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], acc, 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const bf16x8*)(sK + lds_index<D>(krow, 16 * ks + 8 * h));
+        floatx16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qreg[0], zero16, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], acc, 0, 0, 0);
         const bool full = single && k0 >= w_lo && (k0 + 31) <= wq0;
+        if (!full) {
+          const int32_t e = k0 + 4 * h - kshift;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float t = acc[i] * p.sc;
-          if (!full) {
-            const int32_t key = k0 + (i >> 2) * 8 + h * 4 + (i & 3);
-            if (key < start_q || key > qlim) t = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
+            acc[i] = (rel <= span) ? acc[i] : -INFINITY;
           }
-          sv[kb][i] = t;
         }
-      } else {
+        sv[kb] = acc;
+      }
+
+      // ---- online softmax: raw-score max, exp2(s * sc - m * sc) ----------------------
+      float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[kb][i] = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 0 ? !a0 : !a1) continue;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sv[kb][i], sv[kb][i + 1]));
+      }
+      mx = partner_max(mx);
+      const float m_cand = fmaxf(m_run, mx);
+      const bool grow = (m_cand != -INFINITY) && (m_run == -INFINITY || (m_cand - m_run) * sc > kRescaleLog2);
+      if (__builtin_amdgcn_readfirstlane(__ballot(grow) != 0)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_cand) * sc) : 1.f;
+        m_run = grow ? m_cand : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      const float nmsc = (m_run == -INFINITY) ? 0.f : -m_run * sc;
+
+      // ---- P (bf16) per 16-key step, then O^T += V^T P^T ------------------------------
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 0 ? !a0 : !a1) continue;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * kb + jj;
+          short4v vt[DB][2];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            const int vrow0 = 16 * j + 4 * h + ((lane & 15) >> 2);
+            vt[db][0] = tr_read(sV + lds_index<D>(vrow0, col));
+            vt[db][1] = tr_read(sV + lds_index<D>(vrow0 + 8, col));
+          }
+          bf16x2 pp[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][8 * jj + 2 * t], sc, nmsc));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][8 * jj + 2 * t + 1], sc, nmsc));
+            pp[t] = cvt_bf16x2(e0, e1);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, l_run, false);
+          }
+          const bf16x8 pk = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const short8v s8 = __builtin_shufflevector(vt[db][0], vt[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pk, o[db], 0, 0, 0);
+          }
+        }
       }
     }
-    if (!act[0] && !act[1]) continue;
-
-    // ---- online softmax (fp32, base 2) ---------------------------------------------
-    float mx = sv[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    m_run = m_new;
-
-    bf16x8 pk[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float e = __builtin_amdgcn_exp2f(sv[j >> 1][8 * (j & 1) + t] - m_use);
-        l_run += e;
-        pk[j][t] = (__bf16)e;
-      }
-    }
-
-    // ---- O^T += V^T P^T -------------------------------------------------------------
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!act[j >> 1]) continue;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const int vrow0 = 16 * j + 4 * h + ((lane & 15) >> 2);
-        const short4v r0 = tr_read(sV + lds_index<D>(vrow0, col));
-        const short4v r1 = tr_read(sV + lds_index<D>(vrow0 + 8, col));
-        const short8v s8 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, s8);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[j], o[db], 0, 0, 0);
-      }
-    }
+    if (more) lstore(stage ^ 1);
   }
 
   // ---- epilogue: O / l, padding rows (l == 0) -> 0 ------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = partner_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (row_in) {
 #pragma unroll
@@ -296,6 +353,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = w;
       }
   }
+}  // item loop
 }
 
 int heads_per_wg(int64_t group) { return (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1); }
@@ -311,6 +369,8 @@ hipError_t launch_attn(int nh, const AttnParams& prm, unsigned grid, hipStream_t
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+
 
 }  // namespace
 }  // namespace psb
@@ -388,10 +448,13 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   prm.ntile_row = (int32_t)(geo.ntiles / B);
   prm.units = (int32_t)geo.units;
   prm.sc = scale * kLog2e;
-  prm.blk_lo = buf.blk_lo; prm.blk_hi = buf.blk_hi;
-  prm.tile_lo = buf.tile_lo; prm.tile_hi = buf.tile_hi; prm.order = buf.order;
-  const hipError_t e = (D == 128) ? launch_attn<128>((int)geo.nh, prm, (unsigned)geo.grid, s)
-                                  : launch_attn<64>((int)geo.nh, prm, (unsigned)geo.grid, s);
+  prm.items = geo.grid;
+  prm.work = buf.work;
+  // one workgroup per item: the dispatcher starts a new one whenever a slot frees,
+  // which balances the longest-first order better than a fixed persistent split
+  const int64_t grid = geo.grid;
+  const hipError_t e = (D == 128) ? launch_attn<128>((int)geo.nh, prm, (unsigned)grid, s)
+                                  : launch_attn<64>((int)geo.nh, prm, (unsigned)grid, s);
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }
 

@@ -9,37 +9,41 @@ namespace psb {
 constexpr int kRowsPerBlock = 32;  // query rows per wave (one 32-wide MFMA n-block)
 constexpr int kKeysPerTile = 64;   // keys staged in LDS per step
 
+// One row tile of the attention grid, as the kernel reads it (64 bytes, so one
+// workgroup fetches it with a single scalar load).
+struct TileRecord {
+  int32_t b, rt;          // batch row, row tile index
+  int32_t lo, hi;         // key range of the whole tile (hi <= lo: no valid query row)
+  int32_t blk_lo[4];      // key range of each 32-row block of the tile
+  int32_t blk_hi[4];
+  int32_t pad[4];
+};
+static_assert(sizeof(TileRecord) == 64, "tile record is 64 bytes");
+
 // Device tables, carved out of the caller's workspace.
 //   blk_lo/blk_hi [B * nblk]: key range of each 32-row query block (hi <= lo: no valid row)
-//   tile_lo/tile_hi [T]:      union over the NR blocks of a row tile
-//   order [T]:                tile ids, longest key range first
+//   work [T]:                 tile records, longest key range first
 struct ScheduleBuffers {
   int32_t* blk_lo;
   int32_t* blk_hi;
-  int32_t* tile_lo;
-  int32_t* tile_hi;
-  int32_t* order;
+  TileRecord* work;
 };
 
 inline int64_t schedule_nblk(int64_t L) { return (L + kRowsPerBlock - 1) / kRowsPerBlock; }
 inline int64_t schedule_ntiles(int64_t B, int64_t L, int64_t nr) {
   return B * ((schedule_nblk(L) + nr - 1) / nr);
 }
-// bytes of the five tables, each padded to 256 bytes
+inline int64_t pad256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
 inline int64_t schedule_bytes(int64_t B, int64_t L, int64_t nr) {
-  auto pad = [](int64_t n) { return (n * 4 + 255) / 256 * 256; };
-  return 2 * pad(B * schedule_nblk(L)) + 3 * pad(schedule_ntiles(B, L, nr));
+  return 2 * pad256(4 * B * schedule_nblk(L)) + pad256(64 * schedule_ntiles(B, L, nr));
 }
 inline ScheduleBuffers schedule_carve(void* ws, int64_t B, int64_t L, int64_t nr) {
-  auto pad = [](int64_t n) { return (n * 4 + 255) / 256 * 256; };
   char* p = static_cast<char*>(ws);
+  const int64_t nb = pad256(4 * B * schedule_nblk(L));
   ScheduleBuffers s;
-  const int64_t nb = pad(B * schedule_nblk(L)), nt = pad(schedule_ntiles(B, L, nr));
   s.blk_lo = reinterpret_cast<int32_t*>(p);
   s.blk_hi = reinterpret_cast<int32_t*>(p + nb);
-  s.tile_lo = reinterpret_cast<int32_t*>(p + 2 * nb);
-  s.tile_hi = reinterpret_cast<int32_t*>(p + 2 * nb + nt);
-  s.order = reinterpret_cast<int32_t*>(p + 2 * nb + 2 * nt);
+  s.work = reinterpret_cast<TileRecord*>(p + 2 * nb);
   return s;
 }
 

@@ -11,9 +11,9 @@
 // is found by a 64-way search: "doc[p] == doc[q]" is false before start(q) and
 // true from there to q, so each step probes 64 positions and keeps the bracket
 // around the first true one (3 dependent steps for S = 64K).
-// Kernel 2 (one workgroup) merges NR blocks into a row tile, and orders the tiles
-// by descending key-range length (counting sort), so the attention grid starts
-// the longest tiles first.
+// Kernel 2 (one workgroup) merges NR blocks into a row tile record, and orders
+// the records by descending key-range length (counting sort), so the attention
+// workgroups take the longest tiles first.
 #include "psb_internal.h"
 #include "schedule.h"
 
@@ -69,13 +69,34 @@ __device__ inline int32_t tile_iters(int32_t lo, int32_t hi) {
   return hi > lo ? (hi - lo + kKeysPerTile - 1) / kKeysPerTile : 0;
 }
 
+__device__ inline TileRecord make_record(const int32_t* __restrict__ blk_lo, const int32_t* __restrict__ blk_hi,
+                                         int32_t t, int32_t nblk, int32_t nr, int32_t ntile_row) {
+  TileRecord r;
+  r.b = t / ntile_row;
+  r.rt = t % ntile_row;
+  int32_t lo = 0x7fffffff, hi = 0;
+  for (int j = 0; j < 4; ++j) {
+    const int32_t blk = r.rt * nr + j;
+    int32_t l = 0, h = 0;
+    if (j < nr && blk < nblk) {
+      l = blk_lo[r.b * nblk + blk];
+      h = blk_hi[r.b * nblk + blk];
+    }
+    r.blk_lo[j] = l;
+    r.blk_hi[j] = h;
+    if (h > l) { lo = min(lo, l); hi = max(hi, h); }
+  }
+  r.lo = (hi == 0) ? 0 : lo;
+  r.hi = hi;
+  r.pad[0] = r.pad[1] = r.pad[2] = r.pad[3] = 0;
+  return r;
+}
+
 __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t* __restrict__ blk_lo,
                                                                   const int32_t* __restrict__ blk_hi,
                                                                   int32_t B, int32_t nblk, int32_t nr,
                                                                   int32_t ntile_row,
-                                                                  int32_t* __restrict__ tile_lo,
-                                                                  int32_t* __restrict__ tile_hi,
-                                                                  int32_t* __restrict__ order) {
+                                                                  TileRecord* __restrict__ work) {
   __shared__ int32_t hist[kBuckets];
   __shared__ int32_t wsum[kSortThreads / kWave];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
@@ -83,18 +104,8 @@ __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t*
   for (int i = tid; i < kBuckets; i += kSortThreads) hist[i] = 0;
   __syncthreads();
   for (int32_t t = tid; t < T; t += kSortThreads) {
-    const int32_t b = t / ntile_row, rt = t % ntile_row;
-    int32_t lo = 0x7fffffff, hi = 0;
-    for (int32_t j = 0; j < nr; ++j) {
-      const int32_t blk = rt * nr + j;
-      if (blk >= nblk) break;
-      const int32_t l = blk_lo[b * nblk + blk], h = blk_hi[b * nblk + blk];
-      if (h > l) { lo = min(lo, l); hi = max(hi, h); }
-    }
-    if (hi == 0) lo = 0;
-    tile_lo[t] = lo;
-    tile_hi[t] = hi;
-    atomicAdd(&hist[min(tile_iters(lo, hi), kBuckets - 1)], 1);
+    const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
+    atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
   }
   __syncthreads();
   // exclusive scan in DESCENDING bucket order: offset(bk) = sum of hist[bk' > bk].
@@ -117,8 +128,9 @@ __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t*
   hist[kBuckets - 1 - r1] = excl + c0;
   __syncthreads();
   for (int32_t t = tid; t < T; t += kSortThreads) {
-    const int32_t bk = min(tile_iters(tile_lo[t], tile_hi[t]), kBuckets - 1);
-    order[atomicAdd(&hist[bk], 1)] = t;
+    const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
+    const int32_t bk = min(tile_iters(r.lo, r.hi), kBuckets - 1);
+    work[atomicAdd(&hist[bk], 1)] = r;
   }
 }
 
@@ -136,7 +148,7 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
   if (e != hipSuccess) return e;
   const int32_t ntile_row = (nblk + nr - 1) / nr;
   tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
-                                                                buf.tile_lo, buf.tile_hi, buf.order);
+                                                                buf.work);
   return hipGetLastError();
 }
 
