@@ -68,7 +68,8 @@ def build(verbose: bool = False) -> str:
         _run(cmd)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    # --no-undefined: a kernel whose host launch stub went missing fails here, not at load time
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs)
     os.replace(tmp, LIB)
     return LIB
 

@@ -62,26 +62,11 @@ struct AttnParams {
   const TileRecord* work;
 };
 
-// XOR swizzle of the 16-byte chunks of an LDS row (row = D bf16).  D = 128: the
-// 16 rows read together by one b128 K read, and the 4 rows x 4 chunks of one V
-// transpose read, land on distinct banks.  D = 64 (two rows per 256-byte bank
-// window): the same for rows of equal parity.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  } else {
-    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ int lds_index(int row, int col) {  // col in bf16 elements
-  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
-}
-
-__device__ __forceinline__ short4v tr_read(const __bf16* ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(ptr));
+// 16 bytes per lane from a buffer straight into LDS (lane i lands at lds + 16 i).
+// A device-only function: inside a lambda the address-space cast would make the
+// host compilation drop the kernel's launch stub.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -106,254 +91,333 @@ constexpr int kBufferFlags = 0x00020000;
 // it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
 constexpr float kRescaleLog2 = 8.0f;
 
+// LDS tiles (rows padded by 16 bytes, so the 16 rows that one b128 read touches per
+// cycle start on distinct bank groups and every address is a per-lane base plus a
+// compile-time offset):
+//   K   tile: 64 keys x (D + 8) bf16, row-major;
+//   V^T tile: D rows x (64 + 8) bf16.  Row d holds the tile's 64 keys of dimension d;
+//             inside each 16-key group the keys are stored in the order
+//             (0-3, 8-11, 4-7, 12-15), so the 8 keys one lane feeds to a PV MFMA
+//             k-step (keys 16j + 4h + {0..3} and 16j + 8 + 4h + {0..3}, h = lane / 32)
+//             are 16 contiguous bytes.
+__device__ __forceinline__ int vt_pos(int key) {  // key in [0, 64) -> position in a V^T row
+  const int q = (key >> 2) & 3;
+  return (key & ~15) | (((q & 1) << 1 | (q >> 1)) << 2) | (key & 3);
+}
+
 template <int D, int NH>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int NR = kWaves / NH;
   constexpr int KS = D / 16;                              // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;                              // 32-row blocks of O^T
-  constexpr int NCH = D / 8;                              // 16-byte chunks per row
-  constexpr int TILE_ELEMS = kKeysPerTile * D;            // one tensor, one stage
-  constexpr int CPT = TILE_ELEMS / 8 / kThreads;          // 16-byte chunks per thread per tensor
-  static_assert(CPT * kThreads * 8 == TILE_ELEMS, "tile must split evenly");
+  constexpr int NCH = D / 8;                              // 16-byte chunks per K row
+  constexpr int KROW = D + 8;                             // padded K row, elements
+  constexpr int VROW = kKeysPerTile + 8;                  // padded V^T row, elements
+  constexpr int KSTAGE = kKeysPerTile * KROW;             // elements per K stage
+  constexpr int VSTAGE = D * VROW;                        // elements per V^T stage
+  constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;    // 1 KiB wave-wide loads per K tile
+  constexpr int KSEG_ITERS = (KSEGS + kWaves - 1) / kWaves;
+  static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
+  // V staging: each thread loads VK consecutive keys x 8 d (one 16-byte chunk per key)
+  constexpr int VK = (D == 128) ? 4 : 2;
+  constexpr int VKG = kKeysPerTile / VK;                  // key groups per tile
+  static_assert(VKG * (D / 8) == kThreads, "V tile must split into one chunk group per thread");
 
-  // [stage][K, V][64 keys x D], rows XOR-swizzled in 16-byte chunks
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[2][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][KSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = lane >> 5, lr = lane & 31;
-  const int64_t row_bytes = p.kv_ss * 2;
+  // bytes between consecutive keys; a 64-key tile spans < 2^31 bytes (checked on the host)
+  const int32_t row_bytes = (int32_t)(p.kv_ss * 2);
   const bool neg = p.sc < 0.f;
   const float sc = neg ? -p.sc : p.sc;
   const floatx16 zero16 = {};
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
 
+  // K loads: lane `lane` of segment seg fills 16-byte slot seg*64 + lane of the padded
+  // tile; slot -> (row, chunk), pad slots get an offset past every buffer (read as 0)
+  int32_t koff[KSEG_ITERS];
+#pragma unroll
+  for (int j = 0; j < KSEG_ITERS; ++j) {
+    const int slot = (j * kWaves + wv) * 64 + lane;
+    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
+    koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+  }
+  // V staging: thread -> (key group, d chunk)
+  const int vkg = tid % VKG, vdc = tid / VKG;
+  int32_t voff[VK];
+#pragma unroll
+  for (int r = 0; r < VK; ++r) voff[r] = (VK * vkg + r) * row_bytes + 16 * vdc;
+  const int vt_w = 8 * vdc * VROW + vt_pos(VK * vkg);   // V^T write base (element), + i * VROW
+  const int k_rd = lr * KROW + 8 * h;                    // K operand read base (element)
+  const int vt_rd = lr * VROW + 8 * h;                   // V^T operand read base (element)
+
   // workgroup blockIdx.x takes items blockIdx.x, + gridDim.x, ... (one item when the
   // grid covers them all); with 8 kv heads, unit % Hkv == blockIdx.x % 8 keeps each
   // kv head on one XCD
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
-  const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
-  const TileRecord& rec = p.work[rank];
-  const int32_t b = rec.b, rt = rec.rt;
-  // the records come from the caller's workspace: never index with a value that a
-  // plan for this shape cannot have written
-  if (b < 0 || b >= p.B || rt < 0 || rt >= p.ntile_row) continue;
-  const int32_t g = unit % p.Hkv, sub = unit / p.Hkv;
-  const int32_t hq = g * p.group + sub * NH + (wv % NH);
-  const int32_t blk = rt * NR + wv / NH;
-  const int32_t row_local = blk * kRowsPerBlock + lr;
-  const bool row_in = blk < p.nblk && row_local < p.L;
-  const int32_t qpos = p.seq_start + row_local;
-  const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
-  __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
+    const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
+    const TileRecord& rec = p.work[rank];
+    const int32_t b = rec.b, rt = rec.rt;
+    // the records come from the caller's workspace: never index with a value that a
+    // plan for this shape cannot have written
+    if (b < 0 || b >= p.B || rt < 0 || rt >= p.ntile_row) continue;
+    const int32_t g = unit % p.Hkv, sub = unit / p.Hkv;
+    const int32_t hq = g * p.group + sub * NH + (wv % NH);
+    const int32_t blk = rt * NR + wv / NH;
+    const int32_t row_local = blk * kRowsPerBlock + lr;
+    const bool row_in = blk < p.nblk && row_local < p.L;
+    const int32_t qpos = p.seq_start + row_local;
+    const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
+    __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
 
-  if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0
-    if (row_in) {
-      const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = z;
-    }
-    continue;
-  }
-
-  // ---- K/V tile loads: buffer loads (zero past the key range) -> VGPRs -> LDS --------
-  // Staged through registers rather than LDS-direct loads: the transpose reads of V
-  // carry no alias information, so any LDS-writing load still in flight would make
-  // the compiler wait for it before every one of them.
-  const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
-  const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
-  int32_t goff[CPT];   // byte offset of this thread's chunk j within a tile (global)
-  int32_t loff[CPT];   // element offset of the same chunk in an LDS tile (swizzled)
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int ci = tid + j * kThreads;
-    const int row = ci / NCH, c = ci % NCH;
-    goff[j] = (int32_t)(row * row_bytes) + 16 * c;
-    loff[j] = lds_index<D>(row, 8 * c);
-  }
-  u32x4 kr[CPT], vr[CPT];
-  auto gload = [&](int32_t kt) {
-    const int32_t nrows = min(thi - kt, kKeysPerTile);
-    const int32_t nbytes = (int32_t)(nrows * row_bytes);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kt * p.kv_ss), (short)0, nbytes, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kt * p.kv_ss), (short)0, nbytes, kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      kr[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, goff[j], 0, 0);
-      vr[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, goff[j], 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      *(u32x4*)(&smem[stage][0][loff[j]]) = kr[j];
-      *(u32x4*)(&smem[stage][1][loff[j]]) = vr[j];
-    }
-  };
-  gload(tlo);
-
-  // ---- per-wave query block description ------------------------------------------
-  const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
-  const int32_t w_hi = __builtin_amdgcn_readfirstlane(rec.blk_hi[wv / NH]);
-  const int32_t* docrow = p.doc + (int64_t)b * p.S;
-  const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
-  const bool valid = dq != PSB_PAD_DOC_ID;
-  const int32_t dprev = __shfl_up(dq, 1, kWave);
-  const bool flag = (lr == 0) || (dq != dprev);
-  const uint64_t fm = __ballot(flag) & 0xffffffffull;
-  const uint64_t upto = fm & ((2ull << lr) - 1ull);
-  const int rs = 63 - __clzll((long long)upto);             // last run start at or before my row
-  const int32_t wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
-  const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;       // my document's first position
-  // key k is allowed iff 0 <= k - start_q <= span (unsigned compare); padding rows: none
-  const uint32_t span = valid ? (uint32_t)(qpos - start_q) : 0u;
-  const int32_t kshift = valid ? start_q : 0x40000000;       // padding: k - kshift < 0 always
-  const bool single = __builtin_amdgcn_readfirstlane(
-      (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
-
-  // ---- Q^T operand, resident for the whole tile loop (sign-flipped if scale < 0) -------
-  bf16x8 qreg[KS];
-  {
-    const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0
       if (row_in) {
-        qreg[ks] = *(const bf16x8*)(qsrc + 16 * ks + 8 * h);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qreg[ks][t] = (__bf16)0.f;
-      }
-      if (neg) {
-        short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
-        bits ^= (short)0x8000;
-        qreg[ks] = __builtin_bit_cast(bf16x8, bits);
-      }
-    }
-  }
-
-  floatx16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  __syncthreads();  // the previous item's last tile is no longer read from LDS
-  lstore(0);        // waits for the first tile's loads
-
-  int stage = 0;
-  for (int32_t kt = tlo; kt < thi; kt += kKeysPerTile, stage ^= 1) {
-    __syncthreads();  // `stage` written by everyone; stage^1 no longer read
-    const bool more = kt + kKeysPerTile < thi;
-    if (more) gload(kt + kKeysPerTile);
-    const __bf16* sK = smem[stage][0];
-    const __bf16* sV = smem[stage][1];
-
-    const bool a0 = (kt < w_hi) && (kt + 32 > w_lo);
-    const bool a1 = (kt + 32 < w_hi) && (kt + 64 > w_lo);
-    if (a0 || a1) {
-      // ---- S^T = K Q^T per active 32-key block; K operand reads issued first -----------
-      floatx16 sv[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 0 ? !a0 : !a1) continue;
-        const int32_t k0 = kt + 32 * kb;
-        const int krow = 32 * kb + lr;
-        bf16x8 ka[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const bf16x8*)(sK + lds_index<D>(krow, 16 * ks + 8 * h));
-        floatx16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qreg[0], zero16, 0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], acc, 0, 0, 0);
-        const bool full = single && k0 >= w_lo && (k0 + 31) <= wq0;
-        if (!full) {
-          const int32_t e = k0 + 4 * h - kshift;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
-            acc[i] = (rel <= span) ? acc[i] : -INFINITY;
-          }
-        }
-        sv[kb] = acc;
-      }
-
-      // ---- online softmax: raw-score max, exp2(s * sc - m * sc) ----------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 0 ? !a0 : !a1) continue;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sv[kb][i], sv[kb][i + 1]));
-      }
-      mx = partner_max(mx);
-      const float m_cand = fmaxf(m_run, mx);
-      const bool grow = (m_cand != -INFINITY) && (m_run == -INFINITY || (m_cand - m_run) * sc > kRescaleLog2);
-      if (__builtin_amdgcn_readfirstlane(__ballot(grow) != 0)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_cand) * sc) : 1.f;
-        m_run = grow ? m_cand : m_run;
-        l_run *= alpha;
+        const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+          for (int g4 = 0; g4 < 4; ++g4) *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = z;
       }
-      const float nmsc = (m_run == -INFINITY) ? 0.f : -m_run * sc;
+      continue;
+    }
+    const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
 
-      // ---- P (bf16) per 16-key step, then O^T += V^T P^T ------------------------------
+    // ---- tile loads: K global -> LDS directly; V global -> VGPRs -> V^T in LDS ----------
+    const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
+    const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
+    auto issue_k = [&](int st, int32_t kt) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + (int64_t)kt * p.kv_ss), (short)0,
+          min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 0 ? !a0 : !a1) continue;
+      for (int j = 0; j < KSEG_ITERS; ++j) {
+        const int seg = j * kWaves + wv;
+        if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rk, &sK[st][seg * 512], koff[j]);
+      }
+    };
+    u32x4 vreg[VK];
+    auto load_v = [&](int32_t kt) {
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase + (int64_t)kt * p.kv_ss), (short)0,
+          min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * kb + jj;
-          short4v vt[DB][2];
+      for (int r = 0; r < VK; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
+    };
+    auto store_vt = [&](int st) {  // VK keys x 8 d from VGPRs -> 8 rows of the V^T tile
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const int vrow0 = 16 * j + 4 * h + ((lane & 15) >> 2);
-            vt[db][0] = tr_read(sV + lds_index<D>(vrow0, col));
-            vt[db][1] = tr_read(sV + lds_index<D>(vrow0 + 8, col));
-          }
-          bf16x2 pp[4];
+      for (int w = 0; w < 4; ++w) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][8 * jj + 2 * t], sc, nmsc));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][8 * jj + 2 * t + 1], sc, nmsc));
-            pp[t] = cvt_bf16x2(e0, e1);
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, l_run, false);
-          }
-          const bf16x8 pk = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const short8v s8 = __builtin_shufflevector(vt[db][0], vt[db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s8), pk, o[db], 0, 0, 0);
+        for (int e = 0; e < 2; ++e) {
+          __bf16* dst = &sV[st][vt_w + (2 * w + e) * VROW];
+          // v_perm selector: low (e = 0) or high (e = 1) 16 bits of each of two dwords
+          const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+          if constexpr (VK == 4) {
+            uint2 pr;
+            pr.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
+            pr.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
+            *(uint2*)dst = pr;
+          } else {
+            *(uint32_t*)dst = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
           }
         }
       }
-    }
-    if (more) lstore(stage ^ 1);
-  }
+    };
 
-  // ---- epilogue: O / l, padding rows (l == 0) -> 0 ------------------------------------
-  const float l_tot = partner_sum(l_run);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (row_in) {
+    // ---- per-wave query block description ------------------------------------------
+    const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
+    const int32_t* docrow = p.doc + (int64_t)b * p.S;
+    const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
+    const bool valid = dq != PSB_PAD_DOC_ID;
+    const int32_t dprev = __shfl_up(dq, 1, kWave);
+    const bool flag = (lr == 0) || (dq != dprev);
+    const uint64_t fm = __ballot(flag) & 0xffffffffull;
+    const uint64_t upto = fm & ((2ull << lr) - 1ull);
+    const int rs = 63 - __clzll((long long)upto);             // last run start at or before my row
+    const int32_t wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
+    const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;       // my document's first position
+    // key k is allowed iff 0 <= k - start_q <= span (unsigned compare); padding rows: none
+    const uint32_t span = valid ? (uint32_t)(qpos - start_q) : 0u;
+    const int32_t kshift = valid ? start_q : 0x40000000;       // padding: k - kshift < 0 always
+    const bool single = __builtin_amdgcn_readfirstlane(
+        (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
+
+    // ---- Q^T operand, resident for the whole tile loop (sign-flipped if scale < 0) -----
+    bf16x8 qreg[KS];
+    {
+      const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int ks = 0; ks < KS; ++ks) {
+        if (row_in) {
+          qreg[ks] = *(const bf16x8*)(qsrc + 16 * ks + 8 * h);
+        } else {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 w;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) w[t] = (__bf16)(o[db][4 * g4 + t] * inv);
-        *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = w;
+          for (int t = 0; t < 8; ++t) qreg[ks][t] = (__bf16)0.f;
+        }
+        if (neg) {
+          short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
+          bits ^= (short)0x8000;
+          qreg[ks] = __builtin_bit_cast(bf16x8, bits);
+        }
       }
-  }
-}  // item loop
+    }
+
+    floatx16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = zero16;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
+    // operands read four k-steps ahead of their MFMAs
+    auto qk = [&](int st, floatx16 (&s)[2]) {
+      const __bf16* kp = &sK[st][k_rd];
+      constexpr int AH = (KS < 4) ? KS : 4;
+      bf16x8 ka[AH][2];
+#pragma unroll
+      for (int ks = 0; ks < AH; ++ks) {
+        ka[ks][0] = *(const bf16x8*)(kp + 16 * ks);
+        ka[ks][1] = *(const bf16x8*)(kp + 32 * KROW + 16 * ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a0 = ka[ks % AH][0], a1 = ka[ks % AH][1];
+        if (ks + AH < KS) {
+          ka[ks % AH][0] = *(const bf16x8*)(kp + 16 * (ks + AH));
+          ka[ks % AH][1] = *(const bf16x8*)(kp + 32 * KROW + 16 * (ks + AH));
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], ks ? s[0] : zero16, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], ks ? s[1] : zero16, 0, 0, 0);
+      }
+      // keep 2*AH operand reads in flight: LDS latency under load is several MFMA slots
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + 2 * AH < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    // mask (unless both blocks lie inside one document's causal triangle) and row max
+    auto mask_max = [&](int32_t kt, floatx16 (&s)[2]) {
+      const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int32_t e = kt + 32 * kb + 4 * h - kshift;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
+            s[kb][i] = (rel <= span) ? s[kb][i] : -INFINITY;
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(fmaxf(s[0][i], s[0][i + 1]), fmaxf(s[1][i], s[1][i + 1])));
+      return partner_max(mx);
+    };
+    // P = exp2(s * sc - m * sc) as bf16 for 16-key step j; l += its row sums
+    auto softmax_step = [&](const floatx16 (&s)[2], int j, float nmsc, bf16x8& pj) {
+      bf16x2 pp[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t], sc, nmsc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t + 1], sc, nmsc));
+        pp[t] = cvt_bf16x2(e0, e1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, l_run, false);
+      }
+      pj = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                   __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto nmscale = [&]() { return (m_run == -INFINITY) ? 0.f : -m_run * sc; };
+    // softmax(t) fused with PV(t): P for 16-key step j is produced while the MFMAs of
+    // step j-1 run (about 6 VALU ops per MFMA); V^T operands are read one step ahead.
+    // A hard scheduling barrier between steps keeps the interleaving.
+    auto softmax_pv = [&](const floatx16 (&s)[2], int vs) {
+      const float nmsc = nmscale();
+      const __bf16* vp = &sV[vs][vt_rd];
+      bf16x8 pk[4];
+      bf16x8 va[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = *(const bf16x8*)(vp + 32 * db * VROW);
+      softmax_step(s, 0, nmsc, pk[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk[j], o[db], 0, 0, 0);
+          if (j < 3) va[db] = *(const bf16x8*)(vp + 32 * db * VROW + 16 * (j + 1));
+        }
+        if (j < 3) {
+          softmax_step(s, j + 1, nmsc, pk[j + 1]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24 / DB, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // lazy running max: m moves (and O, l are rescaled) only when the tile max exceeds
+    // it by more than 2^8 in the exp2 domain
+    auto grows = [&](float mx, float& m_cand) {
+      m_cand = fmaxf(m_run, mx);
+      return (m_cand != -INFINITY) && (m_run == -INFINITY || (m_cand - m_run) * sc > kRescaleLog2);
+    };
+    auto rescale = [&](bool grow, float m_cand) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_cand) * sc) : 1.f;
+      m_run = grow ? m_cand : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    };
+
+    // ---- tile loop ----------------------------------------------------------------------
+    // Step t reads K(t) from sK[t % 2] (loaded straight into LDS during step t-1) and
+    // V^T(t) from sV[t % 2] (transposed from VGPRs at the end of step t-1).
+    __syncthreads();  // the previous item no longer reads LDS
+    issue_k(0, tlo);
+    load_v(tlo);
+    store_vt(0);
+    for (int32_t t = 0; t < ntiles; ++t) {
+      const int stg = t & 1;
+      const int32_t kt = tlo + t * kKeysPerTile;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t) loads landed
+      __syncthreads();                                   // K(t), V^T(t) visible; stage stg^1 free
+      const bool more = t + 1 < ntiles;
+      if (more) load_v(kt + kKeysPerTile);
+      floatx16 st_s[2];
+      qk(stg, st_s);
+      // K(t+1) goes to LDS only after K(t) has been read: while an LDS-direct load into
+      // sK is in flight the compiler waits for it before every read of sK
+      if (more) issue_k(stg ^ 1, kt + kKeysPerTile);
+      float m_cand;
+      const bool g = grows(mask_max(kt, st_s), m_cand);
+      if (__builtin_amdgcn_readfirstlane(__ballot(g) != 0)) rescale(g, m_cand);
+      softmax_pv(st_s, stg);
+      if (more) store_vt(stg ^ 1);  // V(t+1) -> V^T(t+1) for the next step
+    }
+
+    // ---- epilogue: O / l, padding rows (l == 0) -> 0 ----------------------------------
+    const float l_tot = partner_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (row_in) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = (__bf16)(o[db][4 * g4 + t] * inv);
+          *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = w;
+        }
+    }
+  }  // item loop
 }
 
 int heads_per_wg(int64_t group) { return (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1); }
@@ -430,6 +494,7 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
     if (qs[i] < 0 || kvs[i] < 0 || (qs[i] % 8) != 0 || (kvs[i] % 8) != 0) return PSB_ERR_SHAPE;
   }
   if (qs[2] < D || kvs[2] < D) return PSB_ERR_SHAPE;
+  if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
     return PSB_ERR_INVALID_ARG;
   if (workspace_bytes < (size_t)schedule_bytes(B, L, geo.nr)) return PSB_ERR_CAPACITY;
@@ -517,6 +582,7 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
     if (qs[i] < 0 || kvs[i] < 0 || (qs[i] % 8) != 0 || (kvs[i] % 8) != 0) return PSB_ERR_SHAPE;
   }
   if (qs[2] < D || kvs[2] < D) return PSB_ERR_SHAPE;
+  if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PSB_ERR_INVALID_ARG;
   hipStream_t s = as_stream(stream);
   st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
