@@ -123,7 +123,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int VKG = kKeysPerTile / VK;                  // key groups per tile
   static_assert(VKG * (D / 8) == kThreads, "V tile must split into one chunk group per thread");
 
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][KSTAGE];
+  // Two K stages as separate objects, so the compiler can tell a load in flight into
+  // one from reads of the other (the tile loop is unrolled by two for that reason).
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -187,14 +190,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // ---- tile loads: K global -> LDS directly; V global -> VGPRs -> V^T in LDS ----------
     const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
     const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
-    auto issue_k = [&](int st, int32_t kt) {
+    auto issue_k = [&](__bf16* kbuf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(kbase + (int64_t)kt * p.kv_ss), (short)0,
           min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
       for (int j = 0; j < KSEG_ITERS; ++j) {
         const int seg = j * kWaves + wv;
-        if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rk, &sK[st][seg * 512], koff[j]);
+        if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rk, kbuf + seg * 512, koff[j]);
       }
     };
     u32x4 vreg[VK];
@@ -270,8 +273,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 
     // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
     // operands read four k-steps ahead of their MFMAs
-    auto qk = [&](int st, floatx16 (&s)[2]) {
-      const __bf16* kp = &sK[st][k_rd];
+    auto qk = [&](const __bf16* kbuf, floatx16 (&s)[2]) {
+      const __bf16* kp = kbuf + k_rd;
       constexpr int AH = (KS < 4) ? KS : 4;
       bf16x8 ka[AH][2];
 #pragma unroll
@@ -378,30 +381,36 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     };
 
     // ---- tile loop ----------------------------------------------------------------------
-    // Step t reads K(t) from sK[t % 2] (loaded straight into LDS during step t-1) and
-    // V^T(t) from sV[t % 2] (transposed from VGPRs at the end of step t-1).
+    // Step t reads K(t) from sK0 / sK1 (t even / odd; loaded straight into LDS during step
+    // t-1) and V^T(t) from sV[t % 2] (transposed from VGPRs at the end of step t-1).
     __syncthreads();  // the previous item no longer reads LDS
-    issue_k(0, tlo);
+    issue_k(sK0, tlo);
     load_v(tlo);
     store_vt(0);
-    for (int32_t t = 0; t < ntiles; ++t) {
+    auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext) {
       const int stg = t & 1;
       const int32_t kt = tlo + t * kKeysPerTile;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t) loads landed
-      __syncthreads();                                   // K(t), V^T(t) visible; stage stg^1 free
+      __syncthreads();                                   // K(t), V^T(t) visible; other stages free
       const bool more = t + 1 < ntiles;
-      if (more) load_v(kt + kKeysPerTile);
+      if (more) {
+        issue_k(knext, kt + kKeysPerTile);
+        load_v(kt + kKeysPerTile);
+      }
       floatx16 st_s[2];
-      qk(stg, st_s);
-      // K(t+1) goes to LDS only after K(t) has been read: while an LDS-direct load into
-      // sK is in flight the compiler waits for it before every read of sK
-      if (more) issue_k(stg ^ 1, kt + kKeysPerTile);
+      qk(kcur, st_s);
       float m_cand;
       const bool g = grows(mask_max(kt, st_s), m_cand);
       if (__builtin_amdgcn_readfirstlane(__ballot(g) != 0)) rescale(g, m_cand);
       softmax_pv(st_s, stg);
       if (more) store_vt(stg ^ 1);  // V(t+1) -> V^T(t+1) for the next step
+    };
+    int32_t t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, sK0, sK1);
+      step(t + 1, sK1, sK0);
     }
+    if (t < ntiles) step(t, sK0, sK1);
 
     // ---- epilogue: O / l, padding rows (l == 0) -> 0 ----------------------------------
     const float l_tot = partner_sum(l_run);
