@@ -10,12 +10,14 @@ The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
 
 Default workload: the packed LLM row (B=1, S=L=8192, Hq=32, Hkv=8, D=128,
 uniform[128, 2048] document lengths, 107-token padding tail, seed 2).
-Prints ONE JSON line.  `roofline` describes the attention kernel alone, timed
-with HIP events on the stream it is launched on (K back-to-back launches after
-the timed steps; `kernel_ms_in_step` is the same kernel bracketed inside each
-step); `traffic` is HBM bytes per launch from the committed rocprofv3 counter
-runs, reported only while the kernel source is unchanged; `cpu_baseline` times
-the CPU fp64 oracle on the host cores over the same workload.
+Prints ONE JSON line.  The timed steps carry no events (an event record between
+two launches costs the queue a few microseconds).  `roofline` describes the
+attention kernel alone, timed with HIP events on the stream it is launched on
+around K back-to-back launches after the timed steps; `phase_ms` times the
+boundary calls and the plan the same way.  `traffic` is HBM bytes per launch
+from the committed rocprofv3 counter runs, reported only while the kernel
+source is unchanged; `cpu_baseline` times the CPU fp64 oracle on the host cores
+over the same workload.
 """
 
 from __future__ import annotations
@@ -126,45 +128,50 @@ def main():
                 for b in range(B)]
     qp, kp, vp, dp, op, wp = P(q), P(k), P(v), P(doc_ids), P(out), P(ws)
 
-    def step(ev0=None, ev1=None):
+    def boundary():
         for cu_p, nd, ids_p, scu_p, sn_p in row_ptrs:
             st = lib.psb_doc_ids_from_cu_seqlens(cu_p, nd, S, ids_p, None, sptr)
             assert st == 0, st
             st = lib.psb_segment_cu_seqlens(ids_p, S, scu_p, S + 1, sn_p, sptr)
             assert st == 0, st
+
+    def plan():
         st = lib.psb_blockdiag_attn_plan(dp, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, wp, ws_bytes, sptr)
         assert st == 0, st
-        if ev0 is not None:
-            ev0.record(stream)
+
+    def attention():
         st = lib.psb_blockdiag_attn_fwd_planned(qp, kp, vp, dp, B, Hq, Hkv, L, S, D, None, None, lay.seq_start,
                                                 scale, gqa, op, wp, ws_bytes, None, sptr)
         assert st == 0, st
-        if ev1 is not None:
-            ev1.record(stream)
+
+    def step():
+        boundary()
+        plan()
+        attention()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms_in_step = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-    # The attention kernel alone: the same planned launch K times back to back between
-    # one pair of events on its stream (an event pair around a single launch also
-    # catches the queue's packet gaps, a few microseconds per launch).
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(args.steps):
-        st = lib.psb_blockdiag_attn_fwd_planned(qp, kp, vp, dp, B, Hq, Hkv, L, S, D, None, None, lay.seq_start,
-                                                scale, gqa, op, wp, ws_bytes, None, sptr)
-        assert st == 0, st
-    a1.record(stream)
-    torch.cuda.synchronize(dev)
-    attn_ms = a0.elapsed_time(a1) / args.steps
+
+    def timed(fn, n):
+        # n back-to-back calls between one pair of events on the launch stream
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize(dev)
+        return a0.elapsed_time(a1) / n
+
+    attn_ms = timed(attention, args.steps)
+    phase_ms = {"boundary": round(timed(boundary, args.steps), 5), "plan": round(timed(plan, args.steps), 5),
+                "attention": round(attn_ms, 5)}
     flops = lay.useful_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -179,8 +186,8 @@ def main():
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5),
-                     "kernel_ms_in_step": round(attn_ms_in_step, 5)},
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
+        "phase_ms": phase_ms,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lay, q_cpu, k_cpu, v_cpu)

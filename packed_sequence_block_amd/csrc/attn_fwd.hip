@@ -273,7 +273,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 
     // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
     // operands read four k-steps ahead of their MFMAs
+    // Both MFMA phases (qk and softmax_pv) run at raised wave priority: the other wave on
+    // the SIMD is then usually in its VALU / memory phases, and the arbiter lets the MFMA
+    // issue first instead of leaving the matrix pipe idle.
     auto qk = [&](const __bf16* kbuf, floatx16 (&s)[2]) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       const __bf16* kp = kbuf + k_rd;
       constexpr int AH = (KS < 4) ? KS : 4;
       bf16x8 ka[AH][2];
@@ -299,6 +304,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i + 2 * AH < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     };
     // mask (unless both blocks lie inside one document's causal triangle) and row max
     auto mask_max = [&](int32_t kt, floatx16 (&s)[2]) {
@@ -345,6 +352,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) va[db] = *(const bf16x8*)(vp + 32 * db * VROW);
       softmax_step(s, 0, nmsc, pk[0]);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -363,6 +371,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // lazy running max: m moves (and O, l are rescaled) only when the tile max exceeds
     // it by more than 2^8 in the exp2 domain
