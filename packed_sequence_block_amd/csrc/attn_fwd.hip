@@ -21,11 +21,13 @@
 // softmax runs in fp32 with exp2 (scale * log2 e folded into one multiply), then
 // O^T += V^T P^T with the same MFMA: P comes straight from the lane's own scores
 // (the k-slot order of the MFMA is permuted to match the score layout) and V^T is
-// read from the row-major LDS tile with ds_read_b64_tr_b16.
+// read from the row-major LDS tile with ds_read_b64_tr_b16 (the transposing LDS
+// read), so both K and V go from HBM straight into LDS with buffer_load ... lds.
 //
-// Key blocks outside a wave's range [start of first row's document, last valid
-// row] are skipped; blocks entirely inside one document's causal triangle take no
-// mask; the rest compare each key with the row's [doc start, row] range.
+// A workgroup walks the key tiles of its row tile's range [start of the first valid
+// row's document, last valid row]; tiles entirely inside one document's causal
+// triangle for all of a wave's rows take no mask, the rest compare each key with
+// the row's [doc start, row] range.
 #include <math.h>
 
 
@@ -69,6 +71,13 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
+// two transposing LDS reads (rows r and r + 8) -> the 8 bf16 of one V^T operand
+__device__ __forceinline__ bf16x8 vtr_pair(const __bf16* p, int row8) {
+  const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
+  const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p + row8));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 typedef float float2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x2 cvt_bf16x2(float a, float b) {
   const float2v f = {a, b};
@@ -91,19 +100,12 @@ constexpr int kBufferFlags = 0x00020000;
 // it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
 constexpr float kRescaleLog2 = 8.0f;
 
-// LDS tiles (rows padded by 16 bytes, so the 16 rows that one b128 read touches per
-// cycle start on distinct bank groups and every address is a per-lane base plus a
-// compile-time offset):
-//   K   tile: 64 keys x (D + 8) bf16, row-major;
-//   V^T tile: D rows x (64 + 8) bf16.  Row d holds the tile's 64 keys of dimension d;
-//             inside each 16-key group the keys are stored in the order
-//             (0-3, 8-11, 4-7, 12-15), so the 8 keys one lane feeds to a PV MFMA
-//             k-step (keys 16j + 4h + {0..3} and 16j + 8 + 4h + {0..3}, h = lane / 32)
-//             are 16 contiguous bytes.
-__device__ __forceinline__ int vt_pos(int key) {  // key in [0, 64) -> position in a V^T row
-  const int q = (key >> 2) & 3;
-  return (key & ~15) | (((q & 1) << 1 | (q >> 1)) << 2) | (key & 3);
-}
+// LDS tiles: K and V alike, 64 keys x (D + 8) bf16, row-major.  The 16-byte row
+// padding puts the 16 rows that one b128 K read touches per cycle on distinct bank
+// groups, and every address is a per-lane base plus a compile-time offset.  A PV
+// k-step feeds lane (h = lane / 32) the keys 16j + 4h + {0..3} and 16j + 8 + 4h +
+// {0..3} of one d: two ds_read_b64_tr_b16, each gathering 4 keys x 4 d from 16 lanes'
+// row addresses and handing every lane its own d.
 
 template <int D, int NH>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
@@ -112,22 +114,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int DB = D / 32;                              // 32-row blocks of O^T
   constexpr int NCH = D / 8;                              // 16-byte chunks per K row
   constexpr int KROW = D + 8;                             // padded K row, elements
-  constexpr int VROW = kKeysPerTile + 8;                  // padded V^T row, elements
+  constexpr int VROW = KROW;                               // V tile: same padded rows as K
   constexpr int KSTAGE = kKeysPerTile * KROW;             // elements per K stage
-  constexpr int VSTAGE = D * VROW;                        // elements per V^T stage
+  constexpr int VSTAGE = KSTAGE;
   constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;    // 1 KiB wave-wide loads per K tile
   constexpr int KSEG_ITERS = (KSEGS + kWaves - 1) / kWaves;
   static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
-  // V staging: each thread loads VK consecutive keys x 8 d (one 16-byte chunk per key)
-  constexpr int VK = (D == 128) ? 4 : 2;
-  constexpr int VKG = kKeysPerTile / VK;                  // key groups per tile
-  static_assert(VKG * (D / 8) == kThreads, "V tile must split into one chunk group per thread");
 
-  // Two K stages as separate objects, so the compiler can tell a load in flight into
-  // one from reads of the other (the tile loop is unrolled by two for that reason).
+  // Two K and two V stages as separate objects, so the compiler can tell a load in
+  // flight into one from reads of the other (the tile loop is unrolled by two for that
+  // reason) and issues no wait for it.
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][VSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[VSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = lane >> 5, lr = lane & 31;
@@ -148,13 +148,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
   }
   // V staging: thread -> (key group, d chunk)
-  const int vkg = tid % VKG, vdc = tid / VKG;
-  int32_t voff[VK];
-#pragma unroll
-  for (int r = 0; r < VK; ++r) voff[r] = (VK * vkg + r) * row_bytes + 16 * vdc;
-  const int vt_w = 8 * vdc * VROW + vt_pos(VK * vkg);   // V^T write base (element), + i * VROW
   const int k_rd = lr * KROW + 8 * h;                    // K operand read base (element)
-  const int vt_rd = lr * VROW + 8 * h;                   // V^T operand read base (element)
+  // tr read: lane reads 4 d at row (16 j + 4 h + (lane & 15) / 4) [+ 8], col 32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3)
+  const int vt_rd = (4 * h + ((lane & 15) >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // workgroup blockIdx.x takes items blockIdx.x, + gridDim.x, ... (one item when the
   // grid covers them all); with 8 kv heads, unit % Hkv == blockIdx.x % 8 keeps each
@@ -200,34 +196,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rk, kbuf + seg * 512, koff[j]);
       }
     };
-    u32x4 vreg[VK];
-    auto load_v = [&](int32_t kt) {
+    auto issue_v = [&](__bf16* vbuf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(vbase + (int64_t)kt * p.kv_ss), (short)0,
           min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
-      for (int r = 0; r < VK; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[r], 0, 0);
-    };
-    auto store_vt = [&](int st) {  // VK keys x 8 d from VGPRs -> 8 rows of the V^T tile
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          __bf16* dst = &sV[st][vt_w + (2 * w + e) * VROW];
-          // v_perm selector: low (e = 0) or high (e = 1) 16 bits of each of two dwords
-          const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-          if constexpr (VK == 4) {
-            uint2 pr;
-            pr.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-            pr.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-            *(uint2*)dst = pr;
-          } else {
-            *(uint32_t*)dst = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-          }
-        }
+      for (int j = 0; j < KSEG_ITERS; ++j) {
+        const int seg = j * kWaves + wv;
+        if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rv, vbuf + seg * 512, koff[j]);
       }
     };
-
     // ---- per-wave query block description ------------------------------------------
     const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
     const int32_t* docrow = p.doc + (int64_t)b * p.S;
@@ -343,13 +321,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // softmax(t) fused with PV(t): P for 16-key step j is produced while the MFMAs of
     // step j-1 run (about 6 VALU ops per MFMA); V^T operands are read one step ahead.
     // A hard scheduling barrier between steps keeps the interleaving.
-    auto softmax_pv = [&](const floatx16 (&s)[2], int vs) {
+    auto vtr = [&](const __bf16* ptr) { return vtr_pair(ptr, 8 * VROW); };
+    auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf) {
       const float nmsc = nmscale();
-      const __bf16* vp = &sV[vs][vt_rd];
+      const __bf16* vp = vbuf + vt_rd;
       bf16x8 pk[4];
       bf16x8 va[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[db] = *(const bf16x8*)(vp + 32 * db * VROW);
+      for (int db = 0; db < DB; ++db) va[db] = vtr(vp + 32 * db);
       softmax_step(s, 0, nmsc, pk[0]);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
@@ -358,7 +337,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk[j], o[db], 0, 0, 0);
-          if (j < 3) va[db] = *(const bf16x8*)(vp + 32 * db * VROW + 16 * (j + 1));
+          if (j < 3) va[db] = vtr(vp + 32 * db + 16 * (j + 1) * VROW);
         }
         if (j < 3) {
           softmax_step(s, j + 1, nmsc, pk[j + 1]);
@@ -390,36 +369,33 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     };
 
     // ---- tile loop ----------------------------------------------------------------------
-    // Step t reads K(t) from sK0 / sK1 (t even / odd; loaded straight into LDS during step
-    // t-1) and V^T(t) from sV[t % 2] (transposed from VGPRs at the end of step t-1).
+    // Step t reads K(t), V(t) from sK0 / sV0 (t even) or sK1 / sV1 (t odd), loaded straight
+    // into LDS during step t-1, and starts the loads of K(t+1), V(t+1) into the other pair.
     __syncthreads();  // the previous item no longer reads LDS
     issue_k(sK0, tlo);
-    load_v(tlo);
-    store_vt(0);
-    auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext) {
-      const int stg = t & 1;
+    issue_v(sV0, tlo);
+    auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext, const __bf16* vcur, __bf16* vnext) {
       const int32_t kt = tlo + t * kKeysPerTile;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t) loads landed
-      __syncthreads();                                   // K(t), V^T(t) visible; other stages free
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t), V(t) loads landed
+      __syncthreads();                                   // K(t), V(t) visible; other stages free
       const bool more = t + 1 < ntiles;
       if (more) {
         issue_k(knext, kt + kKeysPerTile);
-        load_v(kt + kKeysPerTile);
+        issue_v(vnext, kt + kKeysPerTile);
       }
       floatx16 st_s[2];
       qk(kcur, st_s);
       float m_cand;
       const bool g = grows(mask_max(kt, st_s), m_cand);
       if (__builtin_amdgcn_readfirstlane(__ballot(g) != 0)) rescale(g, m_cand);
-      softmax_pv(st_s, stg);
-      if (more) store_vt(stg ^ 1);  // V(t+1) -> V^T(t+1) for the next step
+      softmax_pv(st_s, vcur);
     };
     int32_t t = 0;
     for (; t + 1 < ntiles; t += 2) {
-      step(t, sK0, sK1);
-      step(t + 1, sK1, sK0);
+      step(t, sK0, sK1, sV0, sV1);
+      step(t + 1, sK1, sK0, sV1, sV0);
     }
-    if (t < ntiles) step(t, sK0, sK1);
+    if (t < ntiles) step(t, sK0, sK1, sV0, sV1);
 
     // ---- epilogue: O / l, padding rows (l == 0) -> 0 ----------------------------------
     const float l_tot = partner_sum(l_run);
