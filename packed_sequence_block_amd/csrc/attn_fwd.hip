@@ -100,12 +100,16 @@ constexpr int kBufferFlags = 0x00020000;
 // it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
 constexpr float kRescaleLog2 = 8.0f;
 
-// LDS tiles: K and V alike, 64 keys x (D + 8) bf16, row-major.  The 16-byte row
-// padding puts the 16 rows that one b128 K read touches per cycle on distinct bank
-// groups, and every address is a per-lane base plus a compile-time offset.  A PV
-// k-step feeds lane (h = lane / 32) the keys 16j + 4h + {0..3} and 16j + 8 + 4h +
-// {0..3} of one d: two ds_read_b64_tr_b16, each gathering 4 keys x 4 d from 16 lanes'
-// row addresses and handing every lane its own d.
+// LDS tiles, row-major, 64 keys each; every address is a per-lane base plus a
+// compile-time offset.
+//   K: rows of D + 8 bf16.  The 16-byte padding puts the 16 rows that one b128 read
+//      touches per cycle on distinct bank groups.
+//   V: rows of D + 32 bf16.  A PV k-step feeds lane (h = lane / 32) the keys
+//      16j + 4h + {0..3} and 16j + 8 + 4h + {0..3} of one d: two ds_read_b64_tr_b16,
+//      each gathering 4 keys x 4 d from 16 lanes' row addresses and handing every lane
+//      its own d.  One half-wave of such a read covers 4 rows x 64 bytes; a row pitch
+//      of 64 bytes mod 256 puts those on distinct banks (D + 8 or D + 16 leaves 2- to
+//      4-way conflicts).
 
 template <int D, int NH>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
@@ -114,9 +118,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int DB = D / 32;                              // 32-row blocks of O^T
   constexpr int NCH = D / 8;                              // 16-byte chunks per K row
   constexpr int KROW = D + 8;                             // padded K row, elements
-  constexpr int VROW = KROW;                               // V tile: same padded rows as K
+  constexpr int VROW = D + 32;                            // padded V row, elements
   constexpr int KSTAGE = kKeysPerTile * KROW;             // elements per K stage
-  constexpr int VSTAGE = KSTAGE;
+  constexpr int VSTAGE = kKeysPerTile * VROW;             // elements per V stage
+  constexpr int VNCH = VROW / 8;                          // 16-byte slots per V row
+  constexpr int VSEGS = kKeysPerTile * VNCH / 64;
+  constexpr int VSEG_ITERS = (VSEGS + kWaves - 1) / kWaves;
+  static_assert(VSEGS * 64 == kKeysPerTile * VNCH && VSTAGE * 2 == VSEGS * 1024, "V tile segments");
   constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;    // 1 KiB wave-wide loads per K tile
   constexpr int KSEG_ITERS = (KSEGS + kWaves - 1) / kWaves;
   static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
@@ -129,7 +137,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[VSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[VSTAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, kept in an SGPR
   const int h = lane >> 5, lr = lane & 31;
   // bytes between consecutive keys; a 64-key tile spans < 2^31 bytes (checked on the host)
   const int32_t row_bytes = (int32_t)(p.kv_ss * 2);
@@ -138,8 +147,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   const floatx16 zero16 = {};
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
 
-  // K loads: lane `lane` of segment seg fills 16-byte slot seg*64 + lane of the padded
-  // tile; slot -> (row, chunk), pad slots get an offset past every buffer (read as 0)
+  // K and V loads: lane `lane` of segment seg fills 16-byte slot seg*64 + lane of the
+  // padded tile; slot -> (row, chunk); pad slots get an offset past every buffer, so the
+  // load returns 0 and the padding holds zeros
   int32_t koff[KSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < KSEG_ITERS; ++j) {
@@ -147,7 +157,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
     koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
   }
-  // V staging: thread -> (key group, d chunk)
+  int32_t voff[VSEG_ITERS];
+#pragma unroll
+  for (int j = 0; j < VSEG_ITERS; ++j) {
+    const int slot = (j * kWaves + wv) * 64 + lane;
+    const int row = slot / VNCH, ch = slot % VNCH;
+    voff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+  }
   const int k_rd = lr * KROW + 8 * h;                    // K operand read base (element)
   // tr read: lane reads 4 d at row (16 j + 4 h + (lane & 15) / 4) [+ 8], col 32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3)
   const int vt_rd = (4 * h + ((lane & 15) >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -201,9 +217,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
           (void*)(vbase + (int64_t)kt * p.kv_ss), (short)0,
           min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
-      for (int j = 0; j < KSEG_ITERS; ++j) {
+      for (int j = 0; j < VSEG_ITERS; ++j) {
         const int seg = j * kWaves + wv;
-        if (KSEGS % kWaves == 0 || seg < KSEGS) buffer_load_lds16(rv, vbuf + seg * 512, koff[j]);
+        if (VSEGS % kWaves == 0 || seg < VSEGS) buffer_load_lds16(rv, vbuf + seg * 512, voff[j]);
       }
     };
     // ---- per-wave query block description ------------------------------------------
