@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 
     // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
-    // operands read four k-steps ahead of their MFMAs
+    // operands read two k-steps ahead of their MFMAs
     // Both MFMA phases (qk and softmax_pv) run at raised wave priority: the other wave on
     // the SIMD is then usually in its VALU / memory phases, and the arbiter lets the MFMA
     // issue first instead of leaving the matrix pipe idle.
@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       const __bf16* kp = kbuf + k_rd;
-      constexpr int AH = (KS < 4) ? KS : 4;
+      constexpr int AH = (KS < 2) ? KS : 2;
       bf16x8 ka[AH][2];
 #pragma unroll
       for (int ks = 0; ks < AH; ++ks) {

@@ -13,10 +13,25 @@ namespace {
 // ---- doc_ids_from_cu_seqlens ---------------------------------------------------
 // One thread per position: the position's document is the last boundary
 // cu[i] <= p (binary search over the n_docs + 1 boundaries), provided p < cu[n_docs].
+// Each workgroup first copies the boundaries into LDS (when they fit), so the
+// search costs one global load latency instead of one per search step.
 // Threads below n_docs also check that the boundaries are non-decreasing.
+constexpr int kCuLds = 4096;
+
+__device__ inline int32_t last_le(const int32_t* c, int32_t n, int32_t p) {
+  // largest i in [0, n) with c[i] <= p, or -1
+  int32_t lo = 0, hi = n;  // search in [lo, hi)
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (c[mid] <= p) lo = mid + 1; else hi = mid;
+  }
+  return lo - 1;
+}
+
 __global__ void __launch_bounds__(256) doc_ids_kernel(const int32_t* __restrict__ cu, int32_t n_docs,
                                                       int32_t seq_len, int32_t* __restrict__ ids,
                                                       int32_t* __restrict__ status) {
+  __shared__ int32_t scu[kCuLds];
   const int32_t p = blockIdx.x * blockDim.x + threadIdx.x;
   if (status != nullptr) {
     int32_t bits = 0;
@@ -24,14 +39,16 @@ __global__ void __launch_bounds__(256) doc_ids_kernel(const int32_t* __restrict_
     if (p == 0 && (cu[0] < 0 || cu[n_docs] > seq_len)) bits |= PSB_DATA_CU_OUT_OF_RANGE;
     if (bits) atomicOr(status, bits);
   }
-  if (p >= seq_len) return;
-  // largest i in [0, n_docs] with cu[i] <= p, or -1
-  int32_t lo = 0, hi = n_docs + 1;  // search in [lo, hi)
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (cu[mid] <= p) lo = mid + 1; else hi = mid;
+  int32_t i;
+  if (n_docs + 1 <= kCuLds) {  // uniform over the grid
+    for (int32_t j = threadIdx.x; j <= n_docs; j += blockDim.x) scu[j] = cu[j];
+    __syncthreads();
+    if (p >= seq_len) return;
+    i = last_le(scu, n_docs + 1, p);
+  } else {
+    if (p >= seq_len) return;
+    i = last_le(cu, n_docs + 1, p);
   }
-  const int32_t i = lo - 1;
   ids[p] = (i >= 0 && i < n_docs) ? i + 1 : PSB_PAD_DOC_ID;
 }
 

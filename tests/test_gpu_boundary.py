@@ -50,6 +50,19 @@ def test_random_boundaries(psb, seed):
     assert np.array_equal(psb.segment_cu_seqlens(ids[0]).cpu().numpy(), oracle.segment_cu_seqlens(ref[0]))
 
 
+@pytest.mark.parametrize("n", [4094, 4095, 4096, 9000])
+def test_many_documents(psb, n):
+    # boundary lists around the size that the kernel stages in LDS (4096 entries)
+    rng = np.random.default_rng(n)
+    lens = rng.integers(0, 4, size=n)
+    cu = np.concatenate([[3], 3 + np.cumsum(lens)]).astype(np.int32)
+    S = int(cu[-1]) + 11
+    say("boundary many documents n", n, "S", S)
+    ids = psb.doc_ids_from_cu_seqlens(_dev(cu), S, validate=True)
+    ref = oracle.doc_ids_from_cu_seqlens(cu, S)
+    assert np.array_equal(ids.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("S", [0, 1, 2, 15, 16, 17, 16383, 16384, 16385, 40000, 100003])
 def test_segments_of_arbitrary_ids(psb, S):
     rng = np.random.default_rng(S)
