@@ -42,3 +42,4 @@ __all__ = [
     "PAD_DOC_ID", "doc_ids_from_cu_seqlens", "segment_cu_seqlens", "doc_ids_from_seq_lens",
     "allowed_mask", "blockdiag_attn", "blockdiag_attn_loop", "blockdiag_attn_rows", "kv_head_of",
 ]
+from .attention_bwd import blockdiag_attn_bwd, blockdiag_attn_lse
