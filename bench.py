@@ -16,7 +16,8 @@ attention kernel alone, timed with HIP events on the stream it is launched on
 around K back-to-back launches after the timed steps; `phase_ms` times the
 boundary calls and the plan the same way.  `traffic` is HBM bytes per launch
 from the committed rocprofv3 counter runs, reported only while the kernel
-source is unchanged; `cpu_baseline` times the CPU fp64 oracle on the host cores
+source is unchanged; `backward` times the training path's backward (dq, dk, dv)
+on the same workload; `cpu_baseline` times the CPU fp64 oracle on the host cores
 over the same workload.
 """
 
@@ -76,6 +77,38 @@ def cpu_baseline(lay, q, k, v, budget_s: float = 10.0, max_passes: int = 4):
             "sample": f"whole workload x{passes} (all {lay.B} rows, {lay.Hq} heads), {el:.1f} s, fp64 torch-CPU"}
 
 
+def backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
+    """Training path on the same workload: forward with log-sum-exp, then the backward
+    (dq, dk, dv).  Useful flops of the backward are counted as 2.5x the forward's
+    (recomputed Q K^T plus the four gradient products, as attention backward is
+    conventionally counted), over the same allowed pairs."""
+    import torch
+    B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
+    g = torch.Generator().manual_seed(77)
+    dout = torch.randn((B, Hq, L, D), generator=g).to(torch.bfloat16).to(q.device)
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(q, k, v, doc_ids, lay.seq_start, None, lay.enable_gqa)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = ws.numel()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    args = (P(q), P(k), P(v), P(out), P(dout), P(lse), P(doc_ids), B, Hq, Hkv, L, S, D, lay.seq_start,
+            float(D) ** -0.5, 1 if lay.enable_gqa else 0, P(dq), P(dk), P(dv), P(ws), nb, None, sptr)
+
+    def bwd():
+        st = lib.psb_blockdiag_attn_bwd_planned(*args)
+        assert st == 0, st
+
+    for _ in range(3):
+        bwd()
+    torch.cuda.synchronize()
+    ms = timed(bwd, max(5, steps // 2))
+    flops = 2.5 * lay.useful_flops()
+    return {"what": "dq, dk, dv from dout (delta, dq and dk/dv kernels)", "ms": round(ms, 5),
+            "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+            "pct_of_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "flop_convention": "2.5 x forward useful flops"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training-path (backward) timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -189,6 +223,8 @@ def main():
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
         "phase_ms": phase_ms,
     }
+    if not args.no_backward:
+        rec["backward"] = backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lay, q_cpu, k_cpu, v_cpu)
     print(json.dumps(rec), flush=True)

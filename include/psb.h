@@ -168,6 +168,63 @@ psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, const vo
                                           int32_t enable_gqa, void* out, const void* workspace,
                                           size_t workspace_bytes, int32_t* status_word, void* stream);
 
+/*
+ * psb_blockdiag_attn_fwd_planned for training: also writes, per query row, the
+ * log-sum-exp the backward needs (the blockdiag_cp page keeps this path active
+ * while backward recomputes checkpointed forwards).
+ *
+ *   lse   device fp32 [B, Hq, L], contiguous, 4-byte aligned, required:
+ *         lse = log(sum over the row's allowed keys of exp(scale * q.k)), natural
+ *         log, computed from the same bf16-rounded probabilities the output uses
+ *         (relative error of the sum <= 2^-8, so |error| of lse <= 2^-8 + fp32
+ *         rounding); -inf for a row without keys.
+ *
+ * Everything else is as in psb_blockdiag_attn_fwd_planned.
+ */
+psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, const void* v,
+                                              const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                              int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                              const int64_t* kv_strides, int64_t seq_start, float scale,
+                                              int32_t enable_gqa, void* out, float* lse,
+                                              const void* workspace, size_t workspace_bytes,
+                                              int32_t* status_word, void* stream);
+
+/*
+ * Backward of the block-diagonal attention (the blockdiag_cp page keeps this path
+ * active while backward recomputes checkpointed forwards; the glm5_next.cp page
+ * routes K/V gradients back to the rank that owns each shard, so for a query shard
+ * dk / dv hold the contributions of that shard's rows only, to be summed across
+ * ranks).  With s = scale * q.k on the allowed pairs, P = exp(s - lse):
+ *   dv = P^T dout,  dP = dout v^T,  dS = P * (dP - rowsum(dout * out)),
+ *   dq = scale dS k,  dk = scale dS^T q   (dk, dv summed over a kv head's query heads).
+ *
+ * psb_blockdiag_attn_bwd_workspace_size gives the bytes of a workspace that holds
+ * both the tile plan and the backward's per-row table; use it for
+ * psb_blockdiag_attn_plan and psb_blockdiag_attn_fwd_lse_planned too.
+ *
+ * psb_blockdiag_attn_bwd_planned:
+ *   q, k, v, doc_ids, shapes, seq_start, scale, enable_gqa  as in the forward call
+ *                that produced out and lse; q, k, v contiguous.
+ *   out, dout    device bf16 [B, Hq, L, D], contiguous: forward output and its gradient.
+ *   lse          device fp32 [B, Hq, L] from psb_blockdiag_attn_fwd_lse_planned.
+ *   dq           device bf16 [B, Hq, L, D], contiguous (written).
+ *   dk, dv       device bf16 [B, Hkv, S, D], contiguous (written; 0 for keys no row
+ *                of this call attends to).
+ *   workspace    holds the plan for these arguments (psb_blockdiag_attn_plan enqueued
+ *                earlier on this stream), >= psb_blockdiag_attn_bwd_workspace_size bytes,
+ *                16-byte aligned.
+ * Errors as in the forward; every bf16 pointer must be 16-byte aligned and lse
+ * 4-byte aligned (PSB_ERR_INVALID_ARG).  Outputs are fp32-accumulated, rounded once
+ * to bf16; P and dS are rounded to bf16 before the products that consume them.
+ */
+size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t D);
+psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
+                                          const void* dout, const float* lse, const int32_t* doc_ids,
+                                          int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                          int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
+                                          void* dq, void* dk, void* dv, void* workspace,
+                                          size_t workspace_bytes, int32_t* status_word, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

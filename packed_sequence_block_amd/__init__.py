@@ -9,8 +9,10 @@ Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
   rank's contiguous query shard against all delivered keys/values.
 """
 
-from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_fwd, doc_ids_from_cu_seqlens, load,
+from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd, blockdiag_attn_fwd_lse,
+                   bwd_workspace_size, doc_ids_from_cu_seqlens, load,
                    segment_cu_seqlens, status_string, validate_doc_ids, workspace_size)
 
-__all__ = ["PAD_DOC_ID", "PsbError", "blockdiag_attn_fwd", "doc_ids_from_cu_seqlens", "load",
+__all__ = ["PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
+           "bwd_workspace_size", "doc_ids_from_cu_seqlens", "load",
            "segment_cu_seqlens", "status_string", "validate_doc_ids", "workspace_size"]

@@ -46,6 +46,13 @@ SIGNATURES = {
     "psb_blockdiag_attn_fwd_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                 _c_i64, _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp,
                                                 ctypes.c_size_t, _vp, _vp]),
+    "psb_blockdiag_attn_fwd_lse_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                    _c_i64, _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp,
+                                                    _vp, ctypes.c_size_t, _vp, _vp]),
+    "psb_blockdiag_attn_bwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "psb_blockdiag_attn_bwd_planned": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, _vp,
+                                                _vp, ctypes.c_size_t, _vp, _vp]),
 }
 
 _lib = None
@@ -198,3 +205,81 @@ def blockdiag_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_id
         1 if enable_gqa else 0, _ptr(out), _ptr(workspace), need, None, _vp(_stream(q)))
     _check(status, "blockdiag_attn_fwd")
     return out
+
+
+def _check_qkv(q, k, v, contiguous=False):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D bfloat16 tensor")
+        if contiguous and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k/v shape does not match q")
+
+
+def _ids(doc_ids, B, S):
+    ids = doc_ids.reshape(B, -1) if doc_ids.dim() != 2 else doc_ids
+    ids = (ids if ids.dtype == torch.int32 else ids.to(torch.int32)).contiguous()
+    if tuple(ids.shape) != (B, S):
+        raise ValueError(f"doc_ids must be [B, S] = [{B}, {S}]")
+    return ids
+
+
+def bwd_workspace_size(B: int, Hq: int, Hkv: int, L: int, D: int) -> int:
+    return int(load().psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, D))
+
+
+def blockdiag_attn_fwd_lse(q, k, v, doc_ids, seq_start: int = 0, scale: float | None = None,
+                           enable_gqa: bool = False, workspace: torch.Tensor | None = None):
+    """Training forward: ``(out [B,Hq,L,D] bf16, lse [B,Hq,L] fp32, workspace)``.
+
+    All tensors contiguous.  The returned workspace holds the tile plan and is
+    what :func:`blockdiag_attn_bwd` needs for the same arguments.
+    """
+    _need_gpu(q, k, v, doc_ids)
+    _check_qkv(q, k, v, contiguous=True)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    ids = _ids(doc_ids, B, S)
+    need = bwd_workspace_size(B, Hq, Hkv, L, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    gqa = 1 if enable_gqa else 0
+    st = _vp(_stream(q))
+    lib = load()
+    _check(lib.psb_blockdiag_attn_plan(_ptr(ids), B, Hq, Hkv, L, S, D, int(seq_start), gqa, _ptr(workspace),
+                                       need, st), "blockdiag_attn_plan")
+    _check(lib.psb_blockdiag_attn_fwd_lse_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), B, Hq, Hkv, L, S, D,
+                                                  None, None, int(seq_start), sc, gqa, _ptr(out), _ptr(lse),
+                                                  _ptr(workspace), need, None, st),
+           "blockdiag_attn_fwd_lse_planned")
+    return out, lse, workspace
+
+
+def blockdiag_attn_bwd(q, k, v, out, dout, lse, doc_ids, workspace, seq_start: int = 0,
+                       scale: float | None = None, enable_gqa: bool = False):
+    """Gradients ``(dq, dk, dv)`` (bf16) of ``sum(out * dout)``; ``workspace`` from
+    :func:`blockdiag_attn_fwd_lse` with the same arguments."""
+    _need_gpu(q, k, v, out, dout, lse, doc_ids, workspace)
+    _check_qkv(q, k, v, contiguous=True)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like q")
+    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, L] tensor")
+    ids = _ids(doc_ids, B, S)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().psb_blockdiag_attn_bwd_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(ids), B, Hq, Hkv, L, S, D,
+        int(seq_start), sc, 1 if enable_gqa else 0, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+        None, _vp(_stream(q))), "blockdiag_attn_bwd_planned")
+    return dq, dk, dv

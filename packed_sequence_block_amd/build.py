@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpsb.so")
 
-HIP_SOURCES = ["boundary.hip", "schedule.hip", "attn_fwd.hip"]
+HIP_SOURCES = ["boundary.hip", "schedule.hip", "attn_fwd.hip", "attn_bwd.hip"]
 CPP_SOURCES = ["capi.cpp"]
 ARCH = "gfx950"
 

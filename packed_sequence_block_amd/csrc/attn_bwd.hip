@@ -1,0 +1,627 @@
+// Block-diagonal (per-document causal) attention backward for gfx950.
+//
+// The gradients of the forward in attn_fwd.hip (blockdiag_cp page: the packed
+// block-diagonal path stays active while backward recomputes checkpointed
+// forwards; glm5_next.cp page: K/V gradients flow back to the rank that owns each
+// shard, so a shard's call returns the dK / dV of its own rows).  With the
+// forward's log-sum-exp per row, for each (batch, query head):
+//   P  = exp(scale Q K^T - lse)  on the allowed pairs, 0 elsewhere
+//   dP = dO V^T,  delta = rowsum(dO * O),  dS = P * (dP - delta)
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over a kv
+//   head's query heads)
+//
+// Three kernels:
+//   delta_kernel  rowsum(dO * O) in fp32, one 16-lane group per row;
+//   dq_kernel     query-stationary like the forward: a wave owns 32 query rows of one
+//                 head, walks the key tiles of the forward's plan, recomputes S^T and
+//                 dP^T = V dO^T (lane = row), and accumulates dQ^T += K^T dS^T with
+//                 the K^T operand gathered from the K tile by transposing LDS reads;
+//   dkdv_kernel   key-stationary: a wave owns 32 keys of one kv head (K and V held in
+//                 VGPRs as MFMA B operands), a workgroup 128 keys; it walks every query
+//                 head of the group and the 32-row query tiles that can see its keys,
+//                 recomputes S and dP (lane = key), and accumulates dV^T += dO^T P and
+//                 dK^T += Q^T dS with Q^T / dO^T gathered by transposing LDS reads.
+// All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
+// rounded to bf16 for the MFMAs that consume them.
+#include <math.h>
+
+#include "attn_common.h"
+#include "psb_internal.h"
+#include "schedule.h"
+
+namespace psb {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * kWave;
+constexpr int kKeysPerWave = 32;                       // dkdv: keys per wave
+constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgroup
+constexpr int kRowsPerStep = 32;                       // dkdv: query rows per step
+
+struct BwdParams {
+  const __bf16* q;     // [B, Hq, L, D]
+  const __bf16* k;     // [B, Hkv, S, D]
+  const __bf16* v;
+  const __bf16* dout;  // [B, Hq, L, D]
+  const float* lse;    // [B, Hq, L] natural log
+  const float* delta;  // [B, Hq, L]
+  const int32_t* doc;  // [B, S]
+  __bf16* dq;          // [B, Hq, L, D]
+  __bf16* dk;          // [B, Hkv, S, D]
+  __bf16* dv;
+  int32_t B, Hq, Hkv, L, S, seq_start, group;
+  int32_t nblk, ntile_row, units;
+  float scale;         // signed softmax scale
+  float sc;            // |scale| * log2(e)
+  int64_t items;
+  const TileRecord* work;
+};
+
+// ---- delta = rowsum(dO * O) --------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) delta_kernel(const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
+                                                    float* __restrict__ delta, int64_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int part = (int)(gid % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 o = *(const bf16x8*)(out + row * D + 8 * part);
+    const bf16x8 g = *(const bf16x8*)(dout + row * D + 8 * part);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc += (float)o[t] * (float)g[t];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ---- dQ: query-stationary ---------------------------------------------------------
+template <int D, int NH>
+__global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
+  constexpr int NR = kBwdWaves / NH;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NCH = D / 8;
+  constexpr int KROW = D + 8;
+  constexpr int KSTAGE = kKeysPerTile * KROW;
+  constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;
+  constexpr int KSEG_ITERS = (KSEGS + kBwdWaves - 1) / kBwdWaves;
+  static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "tile segments");
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[KSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[KSTAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, lr = lane & 31;
+  const int32_t row_bytes = D * 2;  // contiguous k, v
+  const bool neg = p.scale < 0.f;
+  const float sc = p.sc;  // |scale| * log2(e); Q is sign-flipped for a negative scale
+  const floatx16 zero16 = {};
+
+  int32_t koff[KSEG_ITERS];
+#pragma unroll
+  for (int j = 0; j < KSEG_ITERS; ++j) {
+    const int slot = (j * kBwdWaves + wv) * 64 + lane;
+    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
+    koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+  }
+  const int k_rd = lr * KROW + 8 * h;  // row-major operand read base (A = K or V rows)
+  // transposing read of K^T: key (16 j + 4 h + (lane & 15) / 4) [+ 8], d (32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3))
+  const int kt_rd = (4 * h + ((lane & 15) >> 2)) * KROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
+    const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
+    const TileRecord& rec = p.work[rank];
+    const int32_t b = rec.b, rt = rec.rt;
+    if (b < 0 || b >= p.B || rt < 0 || rt >= p.ntile_row) continue;
+    const int32_t g = unit % p.Hkv, sub = unit / p.Hkv;
+    const int32_t hq = g * p.group + sub * NH + (wv % NH);
+    const int32_t blk = rt * NR + wv / NH;
+    const int32_t row_local = blk * kRowsPerBlock + lr;
+    const bool row_in = blk < p.nblk && row_local < p.L;
+    const int32_t qpos = p.seq_start + row_local;
+    const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
+    const int64_t qrow = ((int64_t)b * p.Hq + hq) * p.L + row_local;
+    __bf16* dq_row = p.dq + qrow * D;
+    if (thi <= tlo) {
+      if (row_in) {
+        const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) *(bf16x4*)(dq_row + 32 * db + 8 * g4 + 4 * h) = z;
+      }
+      continue;
+    }
+    const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
+    const __bf16* kbase = p.k + ((int64_t)b * p.Hkv + g) * p.S * D;
+    const __bf16* vbase = p.v + ((int64_t)b * p.Hkv + g) * p.S * D;
+    auto issue = [&](const __bf16* base, __bf16* buf, int32_t kt) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(base + (int64_t)kt * D), (short)0, min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < KSEG_ITERS; ++j) {
+        const int seg = j * kBwdWaves + wv;
+        if (KSEGS % kBwdWaves == 0 || seg < KSEGS) buffer_load_lds16(r, buf + seg * 512, koff[j]);
+      }
+    };
+
+    // ---- per-wave rows: document range (as in the forward) --------------------------
+    const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
+    const int32_t* docrow = p.doc + (int64_t)b * p.S;
+    const int32_t dqid = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
+    const bool valid = dqid != PSB_PAD_DOC_ID;
+    const int32_t dprev = __shfl_up(dqid, 1, kWave);
+    const bool flag = (lr == 0) || (dqid != dprev);
+    const uint64_t fm = __ballot(flag) & 0xffffffffull;
+    const uint64_t upto = fm & ((2ull << lr) - 1ull);
+    const int rs = 63 - __clzll((long long)upto);
+    const int32_t wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
+    const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;
+    const uint32_t span = valid ? (uint32_t)(qpos - start_q) : 0u;
+    const int32_t kshift = valid ? start_q : 0x40000000;
+    const bool single = __builtin_amdgcn_readfirstlane(
+        (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
+
+    // ---- stationary operands: Q^T (sign-flipped for a negative scale) and dO^T ----------
+    bf16x8 qreg[KS], oreg[KS];
+    {
+      const __bf16* qsrc = p.q + qrow * D;
+      const __bf16* osrc = p.dout + qrow * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (row_in) {
+          qreg[ks] = *(const bf16x8*)(qsrc + 16 * ks + 8 * h);
+          oreg[ks] = *(const bf16x8*)(osrc + 16 * ks + 8 * h);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) { qreg[ks][t] = (__bf16)0.f; oreg[ks][t] = (__bf16)0.f; }
+        }
+        if (neg) {
+          short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
+          bits ^= (short)0x8000;
+          qreg[ks] = __builtin_bit_cast(bf16x8, bits);
+        }
+      }
+    }
+    // exp2 argument offset of the row (rows without keys never produce a P: any finite value)
+    const float lse2 = (valid && row_in) ? p.lse[qrow] * kLog2e : 0.f;
+    const float dlt = row_in ? p.delta[qrow] : 0.f;
+
+    floatx16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = zero16;
+
+    // one 32-key half kb of the tile in kbuf / vbuf
+    auto half = [&](const __bf16* kbuf, const __bf16* vbuf, int32_t kt, int kb) {
+      // S^T and dP^T for keys 32 kb .. 32 kb + 31
+      floatx16 s = zero16, dp = zero16;
+      const __bf16* kp = kbuf + k_rd + 32 * KROW * kb;
+      const __bf16* vp = vbuf + k_rd + 32 * KROW * kb;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(kp + 16 * ks);
+        const bf16x8 c = *(const bf16x8*)(vp + 16 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, oreg[ks], dp, 0, 0, 0);
+      }
+      const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
+      const int32_t e = kt + 32 * kb + 4 * h - kshift;
+      bf16x8 dsk[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          float d2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int i = 8 * j + t + u;
+            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
+            const bool ok = full || rel <= span;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -lse2)) : 0.f;
+            d2[u] = pr * (dp[i] - dlt);
+          }
+          const bf16x2 pk = cvt_bf16x2(d2[0], d2[1]);
+          dsk[j][t] = pk[0];
+          dsk[j][t + 1] = pk[1];
+        }
+      }
+      // dQ^T += K^T dS^T over the two 16-key steps of this half
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const __bf16* tp = kbuf + kt_rd + (32 * kb + 16 * j) * KROW;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = vtr_pair(tp + 32 * db, 8 * KROW);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsk[j], acc[db], 0, 0, 0);
+        }
+      }
+    };
+
+    __syncthreads();  // the previous item no longer reads LDS
+    issue(kbase, sK0, tlo);
+    issue(vbase, sV0, tlo);
+    auto step = [&](int32_t t, const __bf16* kc, __bf16* kn, const __bf16* vc, __bf16* vn) {
+      const int32_t kt = tlo + t * kKeysPerTile;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        issue(kbase, kn, kt + kKeysPerTile);
+        issue(vbase, vn, kt + kKeysPerTile);
+      }
+      half(kc, vc, kt, 0);
+      half(kc, vc, kt, 1);
+    };
+    int32_t t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, sK0, sK1, sV0, sV1);
+      step(t + 1, sK1, sK0, sV1, sV0);
+    }
+    if (t < ntiles) step(t, sK0, sK1, sV0, sV1);
+
+    // ---- epilogue: dQ = scale * dQ^T, bf16 ------------------------------------------------
+    if (row_in) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 w;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) w[u] = (__bf16)(acc[db][4 * g4 + u] * p.scale);
+          *(bf16x4*)(dq_row + 32 * db + 8 * g4 + 4 * h) = w;
+        }
+    }
+  }
+}
+
+// ---- dK, dV: key-stationary -------------------------------------------------------
+// Workgroup item = (b, kv head g, 128 keys [k0, k0 + 128)).  Wave w owns keys
+// k0 + 32 w + (lane % 32).  Key k is seen by the rows r of its document with r >= k:
+// k <= r < end(k), end(k) = one past the last position of k's document (a padding key
+// has no rows).  Rows are local query rows [0, L) at global positions seq_start + r.
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NCH = D / 8;
+  constexpr int QROW = D + 8;                                 // padded Q / dO tile row
+  constexpr int QSLOTS = kRowsPerStep * (NCH + 1);            // 16-byte slots of a tile
+  constexpr int QSEGS = (QSLOTS + 63) / 64;                   // 1 KiB wave-wide loads
+  constexpr int QSEG_ITERS = (QSEGS + kBwdWaves - 1) / kBwdWaves;
+  constexpr int QSTAGE = QSEGS * 512;                         // elements (last segment partly spare)
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ0[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ1[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sO0[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sO1[QSTAGE];
+  __shared__ __attribute__((aligned(16))) float sL[2][kRowsPerStep];   // per row: lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sDl[2][kRowsPerStep];  // per row: delta
+  __shared__ int32_t s_rng[kBwdWaves][2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, lr = lane & 31;
+  const int32_t row_bytes = D * 2;
+  const float ssc = p.scale * kLog2e;  // signed: exp2(s * ssc - lse2) = exp(scale s - lse)
+  const floatx16 zero16 = {};
+  const int32_t nkt = (p.S + kKeysPerItem - 1) / kKeysPerItem;
+
+  int32_t qoff[QSEG_ITERS];
+#pragma unroll
+  for (int j = 0; j < QSEG_ITERS; ++j) {
+    const int slot = (j * kBwdWaves + wv) * 64 + lane;
+    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
+    qoff[j] = (slot < QSLOTS && ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+  }
+  const int a_rd = lr * QROW + 8 * h;  // A = Q / dO rows (lane = row)
+  // transposing read of Q^T / dO^T: row (16 j + 4 h + (lane & 15) / 4) [+ 8], d (32 db + ...)
+  const int t_rd = (4 * h + ((lane & 15) >> 2)) * QROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int64_t item = blockIdx.x; item < (int64_t)p.B * p.Hkv * nkt; item += gridDim.x) {
+    const int32_t kt_i = (int32_t)(item % nkt);
+    const int32_t g = (int32_t)((item / nkt) % p.Hkv);
+    const int32_t b = (int32_t)(item / ((int64_t)nkt * p.Hkv));
+    const int32_t key = kt_i * kKeysPerItem + kKeysPerWave * wv + lr;
+    const bool key_in = key < p.S;
+    const int32_t* docrow = p.doc + (int64_t)b * p.S;
+
+    // ---- this lane's key: the rows that see it -------------------------------------------
+    const int32_t dk_id = key_in ? docrow[key] : PSB_PAD_DOC_ID;
+    // end of the key's document: the next run start inside the wave's 32 keys, else the
+    // end of the run that covers the wave's last key (one 64-way search per wave)
+    const int32_t dnext = __shfl_down(dk_id, 1, kWave);
+    const bool last_of_run = (lr == 31) || (dnext != dk_id);
+    const uint64_t lm = __ballot(last_of_run) & 0xffffffffull;
+    int32_t kend;
+    {
+      const uint64_t from = lm & ~((1ull << lr) - 1ull);       // run ends at or after this key
+      const int e = __ffsll((unsigned long long)from) - 1;      // lane of this run's last key
+      const int32_t wkey0 = __builtin_amdgcn_readfirstlane(kt_i * kKeysPerItem + kKeysPerWave * wv);
+      int32_t tail_end = 0;
+      {
+        // run end after the wave's last key (lane 31); the search is wave-uniform
+        const int32_t q31 = min(wkey0 + 31, p.S - 1);
+        const int32_t x = docrow[q31];
+        int32_t lo = q31, hi = p.S - 1;  // last position of the run lies in [lo, hi]
+        while (lo < hi) {
+          const int32_t step = (hi - lo + kWave - 1) / kWave;
+          int32_t pp = lo + lane * step + 1;
+          if (pp > hi) pp = hi;
+          const uint64_t diff = __ballot(docrow[pp] != x);
+          if (diff == 0) {
+            lo = lo + (kWave - 1) * step + 1;
+            if (lo > hi) lo = hi;
+          } else {
+            const int i = __ffsll((unsigned long long)diff) - 1;
+            const int32_t pi = min(hi, lo + i * step + 1);  // first differing probe
+            hi = pi - 1;
+            lo = (i == 0) ? lo : lo + (i - 1) * step + 1;
+          }
+        }
+        tail_end = lo + 1;
+      }
+      kend = (e < 31) ? wkey0 + e + 1 : tail_end;
+    }
+    const bool key_valid = key_in && dk_id != PSB_PAD_DOC_ID;
+    // local rows [r_lo, r_hi) that see this key
+    int32_t r_lo = key_valid ? max(key, p.seq_start) - p.seq_start : 0;
+    int32_t r_hi = key_valid ? min(kend, p.seq_start + p.L) - p.seq_start : 0;
+    if (r_hi < r_lo) r_hi = r_lo;
+    // wave range: min / max over its keys (empty keys excluded)
+    {
+      int32_t lo_m = (r_hi > r_lo) ? r_lo : 0x7fffffff, hi_m = (r_hi > r_lo) ? r_hi : 0;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        lo_m = min(lo_m, __shfl_xor(lo_m, off, kWave));
+        hi_m = max(hi_m, __shfl_xor(hi_m, off, kWave));
+      }
+      if (lane == 0) { s_rng[wv][0] = lo_m; s_rng[wv][1] = hi_m; }
+    }
+    __syncthreads();
+    int32_t wg_lo = 0x7fffffff, wg_hi = 0;
+#pragma unroll
+    for (int w = 0; w < kBwdWaves; ++w) { wg_lo = min(wg_lo, s_rng[w][0]); wg_hi = max(wg_hi, s_rng[w][1]); }
+    const int32_t w_lo = s_rng[wv][0], w_hi = s_rng[wv][1];
+    // for the mask: row r (local) sees this key iff r - r_lo < r_hi - r_lo (unsigned)
+    const uint32_t kspan = (uint32_t)(r_hi - r_lo);
+
+    // ---- stationary K^T and V^T operands (B operands: lane = key) --------------------------
+    bf16x8 kreg[KS], vreg[KS];
+    {
+      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.S + key;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (key_in) {
+          kreg[ks] = *(const bf16x8*)(p.k + kvrow * D + 16 * ks + 8 * h);
+          vreg[ks] = *(const bf16x8*)(p.v + kvrow * D + 16 * ks + 8 * h);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) { kreg[ks][t] = (__bf16)0.f; vreg[ks][t] = (__bf16)0.f; }
+        }
+      }
+    }
+    floatx16 dka[DB], dva[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { dka[db] = zero16; dva[db] = zero16; }
+
+    const int32_t nsteps_h = (wg_hi > wg_lo) ? (wg_hi - wg_lo + kRowsPerStep - 1) / kRowsPerStep : 0;
+    float pend_l = 0.f, pend_d = 0.f;
+    const int32_t nsteps = nsteps_h * p.group;
+    auto issue = [&](int32_t st, __bf16* qb, __bf16* ob, int stage) {
+      const int32_t hh = st / nsteps_h, rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
+      const int32_t hq = g * p.group + hh;
+      const int64_t base = ((int64_t)b * p.Hq + hq) * p.L + rr;
+      const int32_t nrows = min(kRowsPerStep, p.L - rr);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.q + base * D), (short)0, nrows * row_bytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.dout + base * D), (short)0, nrows * row_bytes, kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < QSEG_ITERS; ++j) {
+        const int seg = j * kBwdWaves + wv;
+        if (QSEGS % kBwdWaves == 0 || seg < QSEGS) {
+          buffer_load_lds16(rq, qb + seg * 512, qoff[j]);
+          buffer_load_lds16(ro, ob + seg * 512, qoff[j]);
+        }
+      }
+      // this step's row lse / delta go to registers now and to LDS at the step's start,
+      // after the wait that the loads above need anyway
+      if (tid < kRowsPerStep) {
+        const bool in = tid < nrows;
+        const float l = in ? p.lse[base + tid] : 0.f;
+        pend_l = (l == -INFINITY) ? 0.f : l * kLog2e;  // rows without keys: P is masked to 0
+        pend_d = in ? p.delta[base + tid] : 0.f;
+      }
+      (void)stage;
+    };
+
+    auto compute = [&](int32_t st, const __bf16* qb, const __bf16* ob, int stage) {
+      const int32_t rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
+      // rows of this step that this wave's keys can see at all
+      if (rr >= w_hi || rr + kRowsPerStep <= w_lo) return;
+      // S = Q K^T and dP = dO V^T: C[row][key], lane = key, rows {8 a + 4 h + c}
+      floatx16 s = zero16, dp = zero16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aq = *(const bf16x8*)(qb + a_rd + 16 * ks);
+        const bf16x8 ao = *(const bf16x8*)(ob + a_rd + 16 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp, 0, 0, 0);
+      }
+      bf16x8 pk[2], dsk[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float4 l4 = *(const float4*)&sL[stage][8 * a + 4 * h];
+        const float4 d4 = *(const float4*)&sDl[stage][8 * a + 4 * h];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int c = 0; c < 4; c += 2) {
+          float pp[2], dd[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int i = 4 * a + c + u;
+            const int32_t r = rr + 8 * a + 4 * h + c + u;
+            const bool ok = (uint32_t)(r - r_lo) < kspan;
+            const float arg = __builtin_fmaf(s[i], ssc, -lv[c + u]);  // Q is not sign-flipped here
+            const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
+            pp[u] = pr;
+            dd[u] = pr * (dp[i] - dv4[c + u]);
+          }
+          const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
+          const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
+          const int j = a >> 1, t = 4 * (a & 1) + c;
+          pk[j][t] = p2[0]; pk[j][t + 1] = p2[1];
+          dsk[j][t] = d2[0]; dsk[j][t + 1] = d2[1];
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-row steps
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const __bf16* to = ob + t_rd + 16 * j * QROW;
+        const __bf16* tq = qb + t_rd + 16 * j * QROW;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ao = vtr_pair(to + 32 * db, 8 * QROW);
+          const bf16x8 aq = vtr_pair(tq + 32 * db, 8 * QROW);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pk[j], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsk[j], dka[db], 0, 0, 0);
+        }
+      }
+    };
+
+    __syncthreads();  // the previous item no longer reads LDS (and s_rng is read)
+    if (nsteps > 0) issue(0, sQ0, sO0, 0);
+    auto step = [&](int32_t st, const __bf16* qc, const __bf16* oc, __bf16* qn, __bf16* on, int stage) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (tid < kRowsPerStep) { sL[stage][tid] = pend_l; sDl[stage][tid] = pend_d; }
+      __syncthreads();
+      if (st + 1 < nsteps) issue(st + 1, qn, on, stage ^ 1);
+      compute(st, qc, oc, stage);
+    };
+    int32_t st = 0;
+    for (; st + 1 < nsteps; st += 2) {
+      step(st, sQ0, sO0, sQ1, sO1, 0);
+      step(st + 1, sQ1, sO1, sQ0, sO0, 1);
+    }
+    if (st < nsteps) step(st, sQ0, sO0, sQ1, sO1, 0);
+
+    // ---- epilogue: C[d][key] -> dk, dv rows (lane = key, 4 consecutive d per store) -------
+    if (key_in) {
+      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.S + key;
+      __bf16* dkr = p.dk + kvrow * D;
+      __bf16* dvr = p.dv + kvrow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 wk, wvv;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            wk[u] = (__bf16)(dka[db][4 * g4 + u] * p.scale);
+            wvv[u] = (__bf16)dva[db][4 * g4 + u];
+          }
+          *(bf16x4*)(dkr + 32 * db + 8 * g4 + 4 * h) = wk;
+          *(bf16x4*)(dvr + 32 * db + 8 * g4 + 4 * h) = wvv;
+        }
+    }
+  }
+}
+
+int heads_per_wg_bwd(int64_t group) { return (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1); }
+
+bool aligned_to(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+int64_t bwd_plan_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
+  const int64_t group = (Hkv > 0 && Hq % Hkv == 0) ? Hq / Hkv : 1;
+  return pad256(schedule_bytes(B, L, kBwdWaves / heads_per_wg_bwd(group)));
+}
+
+template <int D>
+hipError_t launch_bwd(int nh, const BwdParams& prm, const __bf16* out, float* delta, int64_t rows, hipStream_t s) {
+  const int64_t threads = rows * (D / 8);
+  delta_kernel<D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(out, prm.dout, delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned qgrid = (unsigned)prm.items;
+  switch (nh) {
+    case 4: dq_kernel<D, 4><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+    case 2: dq_kernel<D, 2><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+    default: dq_kernel<D, 1><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t kgrid = (int64_t)prm.B * prm.Hkv * ((prm.S + kKeysPerItem - 1) / kKeysPerItem);
+  dkdv_kernel<D><<<dim3((unsigned)kgrid), dim3(kBwdThreads), 0, s>>>(prm);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace psb
+
+using namespace psb;
+
+PSB_API size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t D) {
+  (void)D;
+  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0) return 256;
+  return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + pad256(4 * B * Hq * L));
+}
+
+PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
+                                                  const void* dout, const float* lse, const int32_t* doc_ids,
+                                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                                  int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
+                                                  void* dq, void* dk, void* dv, void* workspace,
+                                                  size_t workspace_bytes, int32_t* status_word, void* stream) {
+  (void)status_word;
+  if (B < 0 || Hq < 0 || Hkv < 0 || L < 0 || S < 0 || D < 0 || seq_start < 0) return PSB_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return PSB_ERR_UNSUPPORTED;
+  if (Hq > 0 && Hkv == 0) return PSB_ERR_SHAPE;
+  if (enable_gqa ? (Hkv > 0 && Hq % Hkv != 0) : (Hq != Hkv)) return PSB_ERR_SHAPE;
+  if (seq_start + L > S) return PSB_ERR_SHAPE;
+  if (L >= INT32_MAX || S >= INT32_MAX || Hq >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || S == 0) return PSB_OK;
+  if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
+  const void* bf[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+  for (const void* ptr : bf)
+    if (ptr == nullptr || !aligned_to(ptr, 16)) return PSB_ERR_INVALID_ARG;
+  if (doc_ids == nullptr || lse == nullptr || !aligned_to(lse, 4)) return PSB_ERR_INVALID_ARG;
+  if (workspace_bytes < psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, D)) return PSB_ERR_CAPACITY;
+  const int64_t group = Hq / Hkv;
+  const int64_t nh = heads_per_wg_bwd(group);
+  const int64_t nr = kBwdWaves / nh;
+  const int64_t ntiles = (L > 0) ? schedule_ntiles(B, L, nr) : 0;
+  const int64_t units = Hq / nh;
+  if (ntiles * units >= INT32_MAX || B * Hkv * ((S + kKeysPerItem - 1) / kKeysPerItem) >= INT32_MAX)
+    return PSB_ERR_SHAPE;
+  const ScheduleBuffers buf = schedule_carve(workspace, B, L, nr);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_plan_bytes(B, Hq, Hkv, L));
+  BwdParams prm;
+  prm.q = static_cast<const __bf16*>(q);
+  prm.k = static_cast<const __bf16*>(k);
+  prm.v = static_cast<const __bf16*>(v);
+  prm.dout = static_cast<const __bf16*>(dout);
+  prm.lse = lse;
+  prm.delta = delta;
+  prm.doc = doc_ids;
+  prm.dq = static_cast<__bf16*>(dq);
+  prm.dk = static_cast<__bf16*>(dk);
+  prm.dv = static_cast<__bf16*>(dv);
+  prm.B = (int32_t)B; prm.Hq = (int32_t)Hq; prm.Hkv = (int32_t)Hkv; prm.L = (int32_t)L; prm.S = (int32_t)S;
+  prm.seq_start = (int32_t)seq_start; prm.group = (int32_t)group;
+  prm.nblk = (int32_t)schedule_nblk(L);
+  prm.ntile_row = (B > 0 && L > 0) ? (int32_t)(ntiles / B) : 0;
+  prm.units = (int32_t)units;
+  prm.scale = scale;
+  prm.sc = fabsf(scale) * kLog2e;
+  prm.items = ntiles * units;
+  prm.work = buf.work;
+  const int64_t rows = B * Hq * L;
+  const hipError_t e = (D == 128)
+      ? launch_bwd<128>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream))
+      : launch_bwd<64>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream));
+  return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
+}

@@ -31,23 +31,17 @@
 #include <math.h>
 
 
+#include "attn_common.h"
 #include "psb_internal.h"
 #include "schedule.h"
 
 namespace psb {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnParams {
   const __bf16* q;
@@ -62,40 +56,9 @@ struct AttnParams {
   float sc;  // softmax scale * log2(e)
   int64_t items;  // row tiles x head units
   const TileRecord* work;
+  float* lse;     // [B, Hq, L] natural-log sum of exp(scale * q.k) per row, or null
 };
 
-// 16 bytes per lane from a buffer straight into LDS (lane i lands at lds + 16 i).
-// A device-only function: inside a lambda the address-space cast would make the
-// host compilation drop the kernel's launch stub.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
-}
-
-// two transposing LDS reads (rows r and r + 8) -> the 8 bf16 of one V^T operand
-__device__ __forceinline__ bf16x8 vtr_pair(const __bf16* p, int row8) {
-  const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
-  const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p + row8));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-typedef float float2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16x2 cvt_bf16x2(float a, float b) {
-  const float2v f = {a, b};
-  return __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
-}
-
-__device__ __forceinline__ float partner_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float partner_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// dword 3 of a raw buffer resource for gfx9-class GPUs (32-bit data format, no
-// swizzle); loads at offsets >= num_records return 0
-constexpr int kBufferFlags = 0x00020000;
 // the running row max is only moved (and O, l rescaled) when a tile's max exceeds
 // it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
 constexpr float kRescaleLog2 = 8.0f;
@@ -187,13 +150,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
     __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
 
-    if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0
+    if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0, lse -inf
       if (row_in) {
         const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) *(bf16x4*)(out_row + 32 * db + 8 * g4 + 4 * h) = z;
+        if (p.lse != nullptr && h == 0) p.lse[((int64_t)b * p.Hq + hq) * p.L + row_local] = -INFINITY;
       }
       continue;
     }
@@ -416,6 +380,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // ---- epilogue: O / l, padding rows (l == 0) -> 0 ----------------------------------
     const float l_tot = partner_sum(l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (p.lse != nullptr && row_in && h == 0) {
+      // sum_k exp(scale s_k) = 2^(m sc) * l in the exp2 domain of the loop (m_run is the
+      // same in both partner lanes); a row without keys gets -inf
+      const float lse2 = (l_tot > 0.f) ? m_run * sc + __log2f(l_tot) : -INFINITY;
+      p.lse[((int64_t)b * p.Hq + hq) * p.L + row_local] = lse2 * 0.69314718055994531f;
+    }
     if (row_in) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -492,7 +462,7 @@ psb_status plan_impl(const int32_t* doc_ids, int64_t B, int64_t L, int64_t S, in
 psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids, int64_t B, int64_t Hq,
                     int64_t Hkv, int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
                     const int64_t* kv_strides, int64_t seq_start, float scale, const AttnGeometry& geo, void* out,
-                    void* workspace, size_t workspace_bytes, hipStream_t s) {
+                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t s) {
   if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
   if (q == nullptr || k == nullptr || v == nullptr || doc_ids == nullptr || out == nullptr || workspace == nullptr)
     return PSB_ERR_INVALID_ARG;
@@ -525,6 +495,7 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   prm.sc = scale * kLog2e;
   prm.items = geo.grid;
   prm.work = buf.work;
+  prm.lse = lse;
   // one workgroup per item: the dispatcher starts a new one whenever a slot frees,
   // which balances the longest-first order better than a fixed persistent split
   const int64_t grid = geo.grid;
@@ -568,7 +539,24 @@ PSB_API psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, 
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
   return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
-                  const_cast<void*>(workspace), workspace_bytes, as_stream(stream));
+                  nullptr, const_cast<void*>(workspace), workspace_bytes, as_stream(stream));
+}
+
+PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, const void* v,
+                                                      const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                                      int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                                      const int64_t* kv_strides, int64_t seq_start, float scale,
+                                                      int32_t enable_gqa, void* out, float* lse,
+                                                      const void* workspace, size_t workspace_bytes,
+                                                      int32_t* status_word, void* stream) {
+  (void)status_word;
+  AttnGeometry geo;
+  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  if (st != PSB_OK) return st;
+  if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
+  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
+                  lse, const_cast<void*>(workspace), workspace_bytes, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
@@ -598,5 +586,5 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
   st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
   if (st != PSB_OK) return st;
   return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
-                  workspace, workspace_bytes, s);
+                  nullptr, workspace, workspace_bytes, s);
 }

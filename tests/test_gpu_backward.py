@@ -1,0 +1,133 @@
+"""GPU training path vs the CPU fp64 oracle: forward log-sum-exp and the backward.
+
+Tolerances, from the arithmetic:
+* lse: the kernel sums the bf16-rounded probabilities (relative rounding <= 2^-8
+  each), so |lse - oracle| <= 2^-8 + fp32 rounding; the test allows 5e-3.
+* dq, dk, dv: every term carries relative rounding of order 2^-8 (P and dS rounded
+  to bf16 before their products, lse as above, the bf16 output O inside
+  rowsum(dO * O), and the final bf16 rounding), so the error scales with the
+  gradient itself: max |gpu - oracle| <= 2e-2 * max |oracle| and mean |gpu - oracle|
+  <= 5e-3 * mean |oracle|, per tensor.
+The oracle gets the same bf16 inputs (q, k, v, dout) upcast exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import oracle_doc_ids, say
+from workloads import make_layout, make_qkv, random_layout
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 5e-3
+REL_MAX = 2e-2
+REL_MEAN = 5e-3
+
+
+@pytest.fixture(scope="module")
+def psb():
+    import packed_sequence_block_amd as m
+    m.load()
+    return m
+
+
+def check_grad(got, ref, what):
+    g = got.detach().float().cpu().double()
+    r = torch.as_tensor(ref, dtype=torch.float64)
+    assert torch.isfinite(g).all(), f"{what}: non-finite"
+    d = (g - r).abs()
+    scale_max = max(r.abs().max().item(), 1e-6)
+    scale_mean = max(r.abs().mean().item(), 1e-9)
+    assert d.max().item() <= REL_MAX * scale_max, f"{what}: max err {d.max().item():.3e} vs {scale_max:.3e}"
+    assert d.mean().item() <= REL_MEAN * scale_mean, f"{what}: mean err {d.mean().item():.3e} vs {scale_mean:.3e}"
+
+
+def run_case(psb, q, k, v, ids, seq_start, scale, gqa, seed, what):
+    dev = "cuda"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    idd = torch.as_tensor(ids, dtype=torch.int32).to(dev)
+    say(what, "B", q.shape[0], "Hq", q.shape[1], "Hkv", k.shape[1], "L", q.shape[2], "S", k.shape[2],
+        "D", q.shape[3], "seq_start", seq_start)
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(qd, kd, vd, idd, seq_start, scale, gqa)
+    # forward output equals the plain forward's
+    plain = psb.blockdiag_attn_fwd(qd, kd, vd, idd, seq_start, scale, gqa)
+    assert torch.equal(out, plain), f"{what}: training forward output differs from the forward"
+    lse_ref = oracle.blockdiag_attn_lse(q, k, ids, seq_start, scale, gqa)
+    lg = lse.cpu().double()
+    fin = torch.isfinite(lse_ref)
+    assert torch.equal(torch.isfinite(lg), fin), f"{what}: lse -inf pattern"
+    assert (lg[fin] - lse_ref[fin]).abs().max().item() <= LSE_TOL if fin.any() else True, f"{what}: lse"
+    g = torch.Generator().manual_seed(seed)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    dq, dk, dv = psb.blockdiag_attn_bwd(qd, kd, vd, out, dout.to(dev), lse, idd, ws, seq_start, scale, gqa)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.blockdiag_attn_bwd(q, k, v, dout, ids, seq_start, scale, gqa)
+    check_grad(dq, rq, what + " dq")
+    check_grad(dk, rk, what + " dk")
+    check_grad(dv, rv, what + " dv")
+    return dq, dk, dv
+
+
+def test_config1(psb):
+    lay = make_layout(1)
+    q, k, v = make_qkv(lay)
+    run_case(psb, q, k, v, oracle_doc_ids(lay), lay.seq_start, None, lay.enable_gqa, 11, "bwd cfg1")
+
+
+SMALL = [
+    # (seed, B, S, L, seq_start, Hq, Hkv, D, pad)
+    (1, 1, 300, 300, 0, 4, 4, 64, 20),
+    (2, 2, 520, 520, 0, 8, 2, 128, 0),
+    (3, 1, 700, 256, 300, 4, 1, 128, 0),
+    (4, 1, 1100, 1100, 0, 16, 1, 64, 37),
+    (5, 1, 640, 200, 190, 8, 8, 128, 5),
+    (6, 3, 260, 260, 0, 2, 2, 64, 60),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"seed{c[0]}" for c in SMALL])
+def test_random_small(psb, case):
+    seed, B, S, L, s0, Hq, Hkv, D, pad = case
+    lay = random_layout(seed, B=B, S=S, L=L, seq_start=s0, Hq=Hq, Hkv=Hkv, D=D, max_pad=pad)
+    q, k, v = make_qkv(lay, seed_base=5000 + 10 * seed)
+    run_case(psb, q, k, v, oracle_doc_ids(lay), s0, None, Hq != Hkv, 100 + seed, f"bwd random-{seed}")
+
+
+def test_negative_scale_and_lead_padding(psb):
+    B, S, H, D = 1, 200, 2, 64
+    ids = np.full((1, S), -1000, dtype=np.int64)
+    ids[0, 13:90] = 4
+    ids[0, 90:170] = 9
+    g = torch.Generator().manual_seed(7)
+    q, k, v = (torch.randn((B, H, S, D), generator=g).to(torch.bfloat16) for _ in range(3))
+    run_case(psb, q, k, v, ids, 0, -0.2, False, 8, "bwd negative scale")
+
+
+def gpu_fwd_bwd(psb, q, k, v, ids, seq_start, dout, gqa):
+    dev = "cuda"
+    qd, kd, vd = q.contiguous().to(dev), k.to(dev), v.to(dev)
+    idd = torch.as_tensor(ids, dtype=torch.int32).to(dev)
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(qd, kd, vd, idd, seq_start, None, gqa)
+    res = psb.blockdiag_attn_bwd(qd, kd, vd, out, dout.contiguous().to(dev), lse, idd, ws, seq_start, None, gqa)
+    torch.cuda.synchronize()
+    return [t.float().cpu() for t in res]
+
+
+def test_shards_sum_to_full(psb):
+    # a partition of the rows into two shards: dq is the concatenation and dk / dv
+    # the sum of the shards' results (the pages' per-rank gradient routing)
+    lay = random_layout(21, B=1, S=600, L=600, seq_start=0, Hq=4, Hkv=2, D=128)
+    q, k, v = make_qkv(lay, seed_base=6000)
+    ids = oracle_doc_ids(lay)
+    g = torch.Generator().manual_seed(31)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    a = 256
+    say("bwd shards at", a)
+    s1 = gpu_fwd_bwd(psb, q[:, :, :a], k, v, ids, 0, dout[:, :, :a], True)
+    s2 = gpu_fwd_bwd(psb, q[:, :, a:], k, v, ids, a, dout[:, :, a:], True)
+    rq, rk, rv = oracle.blockdiag_attn_bwd(q, k, v, dout, ids, 0, None, True)
+    check_grad(torch.cat([s1[0], s2[0]], dim=2), rq, "shards dq")
+    check_grad(s1[1] + s2[1], rk, "shards dk")
+    check_grad(s1[2] + s2[2], rv, "shards dv")
