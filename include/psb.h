@@ -199,8 +199,8 @@ psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, cons
  *   dq = scale dS k,  dk = scale dS^T q   (dk, dv summed over a kv head's query heads).
  *
  * psb_blockdiag_attn_bwd_workspace_size gives the bytes of a workspace that holds
- * both the tile plan and the backward's per-row table; use it for
- * psb_blockdiag_attn_plan and psb_blockdiag_attn_fwd_lse_planned too.
+ * the tile plan, the backward's per-row table and its key-side tile order; use it
+ * for psb_blockdiag_attn_plan and psb_blockdiag_attn_fwd_lse_planned too.
  *
  * psb_blockdiag_attn_bwd_planned:
  *   q, k, v, doc_ids, shapes, seq_start, scale, enable_gqa  as in the forward call
@@ -217,7 +217,8 @@ psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, cons
  * 4-byte aligned (PSB_ERR_INVALID_ARG).  Outputs are fp32-accumulated, rounded once
  * to bf16; P and dS are rounded to bf16 before the products that consume them.
  */
-size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t D);
+size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                             int64_t D);
 psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
                                           const void* dout, const float* lse, const int32_t* doc_ids,
                                           int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,

@@ -49,7 +49,8 @@ SIGNATURES = {
     "psb_blockdiag_attn_fwd_lse_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                     _c_i64, _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp,
                                                     _vp, ctypes.c_size_t, _vp, _vp]),
-    "psb_blockdiag_attn_bwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "psb_blockdiag_attn_bwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                                _c_i64]),
     "psb_blockdiag_attn_bwd_planned": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                                 _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, _vp,
                                                 _vp, ctypes.c_size_t, _vp, _vp]),
@@ -225,8 +226,8 @@ def _ids(doc_ids, B, S):
     return ids
 
 
-def bwd_workspace_size(B: int, Hq: int, Hkv: int, L: int, D: int) -> int:
-    return int(load().psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, D))
+def bwd_workspace_size(B: int, Hq: int, Hkv: int, L: int, S: int, D: int) -> int:
+    return int(load().psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, S, D))
 
 
 def blockdiag_attn_fwd_lse(q, k, v, doc_ids, seq_start: int = 0, scale: float | None = None,
@@ -241,7 +242,7 @@ def blockdiag_attn_fwd_lse(q, k, v, doc_ids, seq_start: int = 0, scale: float | 
     B, Hq, L, D = q.shape
     Hkv, S = k.shape[1], k.shape[2]
     ids = _ids(doc_ids, B, S)
-    need = bwd_workspace_size(B, Hq, Hkv, L, D)
+    need = bwd_workspace_size(B, Hq, Hkv, L, S, D)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)

@@ -55,6 +55,8 @@ struct BwdParams {
   float sc;            // |scale| * log2(e)
   int64_t items;
   const TileRecord* work;
+  const TileRecord* kwork;  // key tiles, longest row range first
+  int32_t nkt;              // key tiles per batch row
 };
 
 // ---- delta = rowsum(dO * O) --------------------------------------------------------
@@ -307,7 +309,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
   const int32_t row_bytes = D * 2;
   const float ssc = p.scale * kLog2e;  // signed: exp2(s * ssc - lse2) = exp(scale s - lse)
   const floatx16 zero16 = {};
-  const int32_t nkt = (p.S + kKeysPerItem - 1) / kKeysPerItem;
+  const int32_t nkt = p.nkt;
+  static_assert(kKeysPerItem == kKeyTile, "key tiles of the plan");
 
   int32_t qoff[QSEG_ITERS];
 #pragma unroll
@@ -320,10 +323,13 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
   // transposing read of Q^T / dO^T: row (16 j + 4 h + (lane & 15) / 4) [+ 8], d (32 db + ...)
   const int t_rd = (4 * h + ((lane & 15) >> 2)) * QROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // item = key-tile rank x kv head; kv head = item % Hkv keeps (with 8 kv heads) one kv
+  // head per XCD
   for (int64_t item = blockIdx.x; item < (int64_t)p.B * p.Hkv * nkt; item += gridDim.x) {
-    const int32_t kt_i = (int32_t)(item % nkt);
-    const int32_t g = (int32_t)((item / nkt) % p.Hkv);
-    const int32_t b = (int32_t)(item / ((int64_t)nkt * p.Hkv));
+    const TileRecord& rec = p.kwork[item / p.Hkv];
+    const int32_t g = (int32_t)(item % p.Hkv);
+    const int32_t b = rec.b, kt_i = rec.rt;
+    if (b < 0 || b >= p.B || kt_i < 0 || kt_i >= nkt) continue;  // workspace from another plan
     const int32_t key = kt_i * kKeysPerItem + kKeysPerWave * wv + lr;
     const bool key_in = key < p.S;
     const int32_t* docrow = p.doc + (int64_t)b * p.S;
@@ -540,20 +546,26 @@ int64_t bwd_plan_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
   return pad256(schedule_bytes(B, L, kBwdWaves / heads_per_wg_bwd(group)));
 }
 
+// workspace: [forward plan][delta: fp32 B*Hq*L][key schedule]
+int64_t bwd_delta_bytes(int64_t B, int64_t Hq, int64_t L) { return pad256(4 * B * Hq * L); }
+
 template <int D>
 hipError_t launch_bwd(int nh, const BwdParams& prm, const __bf16* out, float* delta, int64_t rows, hipStream_t s) {
-  const int64_t threads = rows * (D / 8);
-  delta_kernel<D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(out, prm.dout, delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned qgrid = (unsigned)prm.items;
-  switch (nh) {
-    case 4: dq_kernel<D, 4><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
-    case 2: dq_kernel<D, 2><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
-    default: dq_kernel<D, 1><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+  hipError_t e = hipSuccess;
+  if (rows > 0) {  // L == 0: no query rows, dq is empty and dk / dv are all zero
+    const int64_t threads = rows * (D / 8);
+    delta_kernel<D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(out, prm.dout, delta, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned qgrid = (unsigned)prm.items;
+    switch (nh) {
+      case 4: dq_kernel<D, 4><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+      case 2: dq_kernel<D, 2><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+      default: dq_kernel<D, 1><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t kgrid = (int64_t)prm.B * prm.Hkv * ((prm.S + kKeysPerItem - 1) / kKeysPerItem);
   dkdv_kernel<D><<<dim3((unsigned)kgrid), dim3(kBwdThreads), 0, s>>>(prm);
   return hipGetLastError();
@@ -564,10 +576,11 @@ hipError_t launch_bwd(int nh, const BwdParams& prm, const __bf16* out, float* de
 
 using namespace psb;
 
-PSB_API size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t D) {
+PSB_API size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                                     int64_t D) {
   (void)D;
-  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0) return 256;
-  return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + pad256(4 * B * Hq * L));
+  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0) return 256;
+  return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L) + key_schedule_bytes(B, S));
 }
 
 PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
@@ -585,11 +598,17 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
   if (L >= INT32_MAX || S >= INT32_MAX || Hq >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
   if (B == 0 || Hq == 0 || S == 0) return PSB_OK;
   if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
-  const void* bf[] = {q, k, v, out, dout, dq, dk, dv, workspace};
-  for (const void* ptr : bf)
+  const void* kv_side[] = {k, v, dk, dv, workspace};
+  for (const void* ptr : kv_side)
     if (ptr == nullptr || !aligned_to(ptr, 16)) return PSB_ERR_INVALID_ARG;
-  if (doc_ids == nullptr || lse == nullptr || !aligned_to(lse, 4)) return PSB_ERR_INVALID_ARG;
-  if (workspace_bytes < psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, D)) return PSB_ERR_CAPACITY;
+  if (L > 0) {  // an empty query shard passes empty (possibly null) row tensors
+    const void* q_side[] = {q, out, dout, dq};
+    for (const void* ptr : q_side)
+      if (ptr == nullptr || !aligned_to(ptr, 16)) return PSB_ERR_INVALID_ARG;
+    if (lse == nullptr || !aligned_to(lse, 4)) return PSB_ERR_INVALID_ARG;
+  }
+  if (doc_ids == nullptr) return PSB_ERR_INVALID_ARG;
+  if (workspace_bytes < psb_blockdiag_attn_bwd_workspace_size(B, Hq, Hkv, L, S, D)) return PSB_ERR_CAPACITY;
   const int64_t group = Hq / Hkv;
   const int64_t nh = heads_per_wg_bwd(group);
   const int64_t nr = kBwdWaves / nh;
@@ -598,7 +617,12 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
   if (ntiles * units >= INT32_MAX || B * Hkv * ((S + kKeysPerItem - 1) / kKeysPerItem) >= INT32_MAX)
     return PSB_ERR_SHAPE;
   const ScheduleBuffers buf = schedule_carve(workspace, B, L, nr);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_plan_bytes(B, Hq, Hkv, L));
+  char* wsb = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(wsb + bwd_plan_bytes(B, Hq, Hkv, L));
+  char* kss = wsb + bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L);
+  int32_t* klo = reinterpret_cast<int32_t*>(kss);
+  int32_t* khi = reinterpret_cast<int32_t*>(kss + pad256(4 * key_ntiles(B, S)));
+  TileRecord* kwork = reinterpret_cast<TileRecord*>(kss + 2 * pad256(4 * key_ntiles(B, S)));
   BwdParams prm;
   prm.q = static_cast<const __bf16*>(q);
   prm.k = static_cast<const __bf16*>(k);
@@ -619,7 +643,12 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
   prm.sc = fabsf(scale) * kLog2e;
   prm.items = ntiles * units;
   prm.work = buf.work;
+  prm.kwork = kwork;
+  prm.nkt = (int32_t)((S + kKeyTile - 1) / kKeyTile);
   const int64_t rows = B * Hq * L;
+  if (launch_key_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, klo, khi, kwork,
+                          as_stream(stream)) != hipSuccess)
+    return PSB_ERR_HIP;
   const hipError_t e = (D == 128)
       ? launch_bwd<128>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream))
       : launch_bwd<64>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream));

@@ -134,6 +134,55 @@ __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t*
   }
 }
 
+// ---- key side (backward dK / dV) -----------------------------------------------------
+// One wave per tile of kKeyTile keys: the local query rows that see any of its keys,
+// [max(first valid key, seq_start), min(end of the last valid key's document,
+// seq_start + L)) - seq_start (key k is seen by the rows of its document at or after
+// k; the run end is found by a 64-way search).  Empty tiles get (0, 0).
+__global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restrict__ doc_ids, int32_t S, int32_t L,
+                                                        int32_t seq_start, int32_t nkt, int32_t total,
+                                                        int32_t* __restrict__ klo, int32_t* __restrict__ khi) {
+  const int32_t wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (wid >= total) return;
+  const int32_t b = wid / nkt, kt = wid % nkt;
+  const int32_t* row = doc_ids + (int64_t)b * S;
+  const int32_t k0 = kt * kKeyTile;
+  static_assert(kKeyTile == 2 * kWave, "two keys per lane");
+  const int32_t ka = k0 + lane, kb = k0 + kWave + lane;
+  const bool va = ka < S && row[ka] != PSB_PAD_DOC_ID;
+  const bool vb = kb < S && row[kb] != PSB_PAD_DOC_ID;
+  const uint64_t ma = __ballot(va), mb = __ballot(vb);
+  if ((ma | mb) == 0) {
+    if (lane == 0) { klo[wid] = 0; khi[wid] = 0; }
+    return;
+  }
+  const int32_t kf = ma ? k0 + __ffsll((unsigned long long)ma) - 1 : k0 + kWave + __ffsll((unsigned long long)mb) - 1;
+  const int32_t kl = mb ? k0 + kWave + 63 - __clzll((long long)mb) : k0 + 63 - __clzll((long long)ma);
+  // last position of kl's run: in [lo, hi]
+  const int32_t x = row[kl];
+  int32_t lo = kl, hi = S - 1;
+  while (lo < hi) {
+    const int32_t step = (hi - lo + kWave - 1) / kWave;
+    int32_t p = lo + lane * step + 1;
+    if (p > hi) p = hi;
+    const uint64_t diff = __ballot(row[p] != x);
+    if (diff == 0) {
+      lo = min(lo + (kWave - 1) * step + 1, hi);
+    } else {
+      const int32_t i = __ffsll((unsigned long long)diff) - 1;
+      const int32_t pi = min(hi, lo + i * step + 1);
+      hi = pi - 1;
+      lo = (i == 0) ? lo : lo + (i - 1) * step + 1;
+    }
+  }
+  const int32_t r0 = max(kf, seq_start), r1 = min(lo + 1, seq_start + L);
+  if (lane == 0) {
+    klo[wid] = (r1 > r0) ? r0 - seq_start : 0;
+    khi[wid] = (r1 > r0) ? r1 - seq_start : 0;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
@@ -149,6 +198,24 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
   const int32_t ntile_row = (nblk + nr - 1) / nr;
   tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
                                                                 buf.work);
+  return hipGetLastError();
+}
+
+}  // namespace psb
+
+namespace psb {
+
+hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
+                               int32_t* klo, int32_t* khi, TileRecord* work, hipStream_t stream) {
+  const int32_t nkt = (S + kKeyTile - 1) / kKeyTile;
+  const int32_t total = B * nkt;
+  const int waves_per_wg = 256 / kWave;
+  const int32_t grid = (total + waves_per_wg - 1) / waves_per_wg;
+  key_range_kernel<<<dim3(grid), dim3(256), 0, stream>>>(doc_ids, S, L, seq_start, nkt, total, klo, khi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // longest row range first, as for the query side (records with nr = 1: one key tile each)
+  tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(klo, khi, B, nkt, 1, nkt, work);
   return hipGetLastError();
 }
 

@@ -131,3 +131,18 @@ def test_shards_sum_to_full(psb):
     check_grad(torch.cat([s1[0], s2[0]], dim=2), rq, "shards dq")
     check_grad(s1[1] + s2[1], rk, "shards dk")
     check_grad(s1[2] + s2[2], rv, "shards dv")
+
+
+def test_no_query_rows_gives_zero_kv_gradients(psb):
+    # an empty query shard: dq is empty and no key receives a gradient
+    dev = "cuda"
+    g = torch.Generator().manual_seed(3)
+    q = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=dev)
+    k, v = (torch.randn((1, 2, 50, 64), generator=g).to(torch.bfloat16).to(dev) for _ in range(2))
+    ids = torch.ones((1, 50), dtype=torch.int32, device=dev)
+    say("bwd empty shard")
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(q, k, v, ids, 20, None, False)
+    dq, dk, dv = psb.blockdiag_attn_bwd(q, k, v, out, torch.zeros_like(q), lse, ids, ws, 20, None, False)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
