@@ -20,7 +20,8 @@
 //                 VGPRs as MFMA B operands), a workgroup 128 keys; it walks every query
 //                 head of the group and the 32-row query tiles that can see its keys,
 //                 recomputes S and dP (lane = key), and accumulates dV^T += dO^T P and
-//                 dK^T += Q^T dS with Q^T / dO^T gathered by transposing LDS reads.
+//                 dK^T += Q^T dS with Q^T / dO^T gathered by transposing LDS reads;
+//                 a step stages 64 rows at D = 128 (two independent 32-row halves).
 // All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the MFMAs that consume them.
 #include <math.h>
@@ -36,7 +37,6 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 constexpr int kKeysPerWave = 32;                       // dkdv: keys per wave
 constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgroup
-constexpr int kRowsPerStep = 32;                       // dkdv: query rows per step
 
 struct BwdParams {
   const __bf16* q;     // [B, Hq, L, D]
@@ -287,6 +287,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 // has no rows).  Rows are local query rows [0, L) at global positions seq_start + r.
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
+  // query rows per step: 64 (two independent 32-row halves) at D = 128, where the extra
+  // independent MFMA work pays; 32 at D = 64, where it did not (measured)
+  constexpr int kRowsPerStep = (D == 128) ? 64 : 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
@@ -444,57 +447,71 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
       (void)stage;
     };
 
+    // one step: kRowsPerStep rows as NHALF independent 32-row halves, so the MFMAs of one
+    // half can run while the other's probabilities are computed
+    constexpr int NHALF = kRowsPerStep / 32;
     auto compute = [&](int32_t st, const __bf16* qb, const __bf16* ob, int stage) {
       const int32_t rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
       // rows of this step that this wave's keys can see at all
       if (rr >= w_hi || rr + kRowsPerStep <= w_lo) return;
       // S = Q K^T and dP = dO V^T: C[row][key], lane = key, rows {8 a + 4 h + c}
-      floatx16 s = zero16, dp = zero16;
+      floatx16 s[NHALF], dp[NHALF];
+#pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf) { s[hf] = zero16; dp[hf] = zero16; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = *(const bf16x8*)(qb + a_rd + 16 * ks);
-        const bf16x8 ao = *(const bf16x8*)(ob + a_rd + 16 * ks);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp, 0, 0, 0);
-      }
-      bf16x8 pk[2], dsk[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float4 l4 = *(const float4*)&sL[stage][8 * a + 4 * h];
-        const float4 d4 = *(const float4*)&sDl[stage][8 * a + 4 * h];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int c = 0; c < 4; c += 2) {
-          float pp[2], dd[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 4 * a + c + u;
-            const int32_t r = rr + 8 * a + 4 * h + c + u;
-            const bool ok = (uint32_t)(r - r_lo) < kspan;
-            const float arg = __builtin_fmaf(s[i], ssc, -lv[c + u]);  // Q is not sign-flipped here
-            const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
-            pp[u] = pr;
-            dd[u] = pr * (dp[i] - dv4[c + u]);
-          }
-          const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
-          const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
-          const int j = a >> 1, t = 4 * (a & 1) + c;
-          pk[j][t] = p2[0]; pk[j][t + 1] = p2[1];
-          dsk[j][t] = d2[0]; dsk[j][t + 1] = d2[1];
+        for (int hf = 0; hf < NHALF; ++hf) {
+          const bf16x8 aq = *(const bf16x8*)(qb + a_rd + 32 * hf * QROW + 16 * ks);
+          const bf16x8 ao = *(const bf16x8*)(ob + a_rd + 32 * hf * QROW + 16 * ks);
+          s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
+          dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[hf], 0, 0, 0);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-row steps
+      bf16x8 pk[NHALF][2], dsk[NHALF][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const __bf16* to = ob + t_rd + 16 * j * QROW;
-        const __bf16* tq = qb + t_rd + 16 * j * QROW;
+      for (int hf = 0; hf < NHALF; ++hf) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ao = vtr_pair(to + 32 * db, 8 * QROW);
-          const bf16x8 aq = vtr_pair(tq + 32 * db, 8 * QROW);
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pk[j], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsk[j], dka[db], 0, 0, 0);
+        for (int a = 0; a < 4; ++a) {
+          const float4 l4 = *(const float4*)&sL[stage][32 * hf + 8 * a + 4 * h];
+          const float4 d4 = *(const float4*)&sDl[stage][32 * hf + 8 * a + 4 * h];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int c = 0; c < 4; c += 2) {
+            float pp[2], dd[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int i = 4 * a + c + u;
+              const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
+              const bool ok = (uint32_t)(r - r_lo) < kspan;
+              const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
+              const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
+              pp[u] = pr;
+              dd[u] = pr * (dp[hf][i] - dv4[c + u]);
+            }
+            const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
+            const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
+            const int j = a >> 1, t = 4 * (a & 1) + c;
+            pk[hf][j][t] = p2[0]; pk[hf][j][t + 1] = p2[1];
+            dsk[hf][j][t] = d2[0]; dsk[hf][j][t + 1] = d2[1];
+          }
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 16-row k-steps
+#pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const __bf16* to = ob + t_rd + (32 * hf + 16 * j) * QROW;
+          const __bf16* tq = qb + t_rd + (32 * hf + 16 * j) * QROW;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 ao = vtr_pair(to + 32 * db, 8 * QROW);
+            const bf16x8 aq = vtr_pair(tq + 32 * db, 8 * QROW);
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pk[hf][j], dva[db], 0, 0, 0);
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsk[hf][j], dka[db], 0, 0, 0);
+          }
         }
       }
     };
