@@ -7,12 +7,17 @@ Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
 * :func:`blockdiag_attn_fwd` — attention with the per-document causal mask,
   for a packed row (``seq_start = 0``, ``L = S``) or one context-parallel
   rank's contiguous query shard against all delivered keys/values.
+* :func:`blockdiag_attn_fwd_lse` / :func:`blockdiag_attn_bwd` — the training
+  path (forward with per-row log-sum-exp, then dq, dk, dv);
+  :func:`blockdiag_attention` wraps both as a torch autograd function.
 """
 
 from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd, blockdiag_attn_fwd_lse,
                    bwd_workspace_size, doc_ids_from_cu_seqlens, load,
                    segment_cu_seqlens, status_string, validate_doc_ids, workspace_size)
 
-__all__ = ["PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
+from .autograd import blockdiag_attention
+
+__all__ = ["blockdiag_attention", "PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
            "bwd_workspace_size", "doc_ids_from_cu_seqlens", "load",
            "segment_cu_seqlens", "status_string", "validate_doc_ids", "workspace_size"]

@@ -146,3 +146,22 @@ def test_no_query_rows_gives_zero_kv_gradients(psb):
     torch.cuda.synchronize()
     assert dq.numel() == 0
     assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
+
+
+def test_autograd_function(psb):
+    # loss.backward() through the autograd wrapper gives the oracle's gradients
+    lay = random_layout(41, B=1, S=400, L=400, seq_start=0, Hq=4, Hkv=2, D=64)
+    q, k, v = make_qkv(lay, seed_base=7000)
+    ids = oracle_doc_ids(lay)
+    g = torch.Generator().manual_seed(9)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    dev = "cuda"
+    qd, kd, vd = (t.to(dev).requires_grad_(True) for t in (q, k, v))
+    say("bwd autograd")
+    out = psb.blockdiag_attention(qd, kd, vd, torch.as_tensor(ids, dtype=torch.int32).to(dev), 0, None, True)
+    (out.float() * dout.to(dev).float()).sum().backward()
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.blockdiag_attn_bwd(q, k, v, dout, ids, 0, None, True)
+    check_grad(qd.grad, rq, "autograd dq")
+    check_grad(kd.grad, rk, "autograd dk")
+    check_grad(vd.grad, rv, "autograd dv")
