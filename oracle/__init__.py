@@ -34,7 +34,8 @@ independently of this code (library routines, closed forms, brute force,
 worked examples under ``tests/golden``).
 """
 
-from .boundary import PAD_DOC_ID, doc_ids_from_cu_seqlens, segment_cu_seqlens, doc_ids_from_seq_lens
+from .boundary import (PAD_DOC_ID, doc_ids_from_cu_seqlens, doc_ids_from_seq_lens, document_positions_valid,
+                       segment_cu_seqlens)
 from .attention import (allowed_mask, blockdiag_attn, blockdiag_attn_loop, blockdiag_attn_rows,
                         kv_head_of)
 

@@ -83,3 +83,40 @@ def segment_cu_seqlens(doc_ids_row) -> np.ndarray:
     if n > 0:
         cu.append(n)
     return np.asarray(cu, dtype=np.int32)
+
+
+def document_positions_valid(keep, positions) -> np.ndarray:
+    """Per row: do the logical positions follow the document rule?  ``[batch]`` bool.
+
+    inkling2 ``context_parallel`` page, ``validate_document_positions``: inside a
+    document positions grow by one, a new document starts at zero, a contiguous
+    shard may begin partway through a document (so the first kept token may carry
+    any offset, also after left padding), and a gap never resumes an earlier
+    document.  Reading, for the kept tokens of a row in order:
+      * the first kept token: position >= 0;
+      * a kept token right after a kept token: previous + 1 (same document) or 0
+        (a new document);
+      * a kept token after one or more dropped tokens: 0.
+    """
+    keep = np.asarray(keep).astype(bool)
+    pos = np.asarray(positions).astype(np.int64)
+    if keep.shape != pos.shape or keep.ndim != 2:
+        raise ValueError("keep and positions must both be [batch, sequence]")
+    ok = np.ones(keep.shape[0], dtype=bool)
+    for b in range(keep.shape[0]):
+        seen = False
+        for p in range(keep.shape[1]):
+            if not keep[b, p]:
+                continue
+            x = int(pos[b, p])
+            if not seen:
+                good = x >= 0
+            elif keep[b, p - 1]:
+                good = x == int(pos[b, p - 1]) + 1 or x == 0
+            else:
+                good = x == 0
+            if not good:
+                ok[b] = False
+                break
+            seen = True
+    return ok

@@ -95,3 +95,57 @@ def test_seq_lens_variant_matches_cu_variant():
     np.testing.assert_array_equal(ids[1], oracle.doc_ids_from_cu_seqlens([0, 1, 2, 6], 7)[0])
     with pytest.raises(ValueError):
         oracle.doc_ids_from_seq_lens(np.asarray([[5, 5]]), 7)
+
+
+# ---- document positions (inkling2 context_parallel page, validate_document_positions) ----
+
+POS_CASES = [
+    # (keep, positions, valid) — hand-derived from the rule
+    ([1, 1, 1, 1, 1, 1], [0, 1, 2, 0, 1, 2], True),          # two documents
+    ([0, 0, 1, 1, 1, 1], [9, 9, 7, 8, 0, 1], True),          # shard starts mid-document after left padding
+    ([1, 1, 0, 0, 1, 1], [0, 1, 5, 5, 0, 1], True),          # dropped tokens, then a new document
+    ([1, 1, 0, 1, 1, 1], [0, 1, 0, 2, 3, 4], False),         # a gap resumes the old document
+    ([1, 1, 1, 1], [0, 1, 3, 4], False),                     # skipped increment
+    ([1, 1, 1, 1], [4, 5, 2, 3], False),                     # reset to a non-zero position
+    ([1, 1, 1], [-1, 0, 1], False),                          # negative first position
+    ([0, 0, 0], [3, -2, 7], True),                           # nothing kept
+    ([1, 0, 1], [5, 0, 0], True),                            # gap then reset
+]
+
+
+@pytest.mark.parametrize("keep,pos,valid", POS_CASES)
+def test_document_positions_hand_cases(keep, pos, valid):
+    got = oracle.document_positions_valid(np.asarray([keep]), np.asarray([pos]))
+    assert got.tolist() == [valid]
+
+
+def _layout_positions(rng, S):
+    """Positions built from document lengths with dropped tokens between documents:
+    valid by construction; the first document may start mid-way (a shard)."""
+    keep = np.zeros(S, dtype=bool)
+    pos = np.full(S, 77, dtype=np.int64)
+    p = int(rng.integers(0, 4))
+    first = True
+    while p < S:
+        n = int(rng.integers(1, 9))
+        off = int(rng.integers(0, 5)) if first else 0
+        for i in range(min(n, S - p)):
+            keep[p + i] = True
+            pos[p + i] = off + i
+        p += n + int(rng.integers(0, 3))
+        first = False
+    return keep, pos
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_document_positions_constructed_and_broken(seed):
+    rng = np.random.default_rng(seed)
+    keep, pos = _layout_positions(rng, 40)
+    assert oracle.document_positions_valid(keep[None], pos[None]).tolist() == [True]
+    kept = np.nonzero(keep)[0]
+    if kept.size > 1:
+        bad = pos.copy()
+        i = int(rng.choice(kept[1:]))
+        # neither 0 nor previous + 1 (after a kept token), not 0 after a gap
+        bad[i] = bad[i - 1] + 2 if keep[i - 1] else 5
+        assert oracle.document_positions_valid(keep[None], bad[None]).tolist() == [False]
