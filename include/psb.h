@@ -48,6 +48,8 @@ typedef int32_t psb_status;
 #define PSB_DATA_CU_NOT_MONOTONE 1   /* cu_seqlens decreases somewhere */
 #define PSB_DATA_CU_OUT_OF_RANGE 2   /* cu_seqlens[0] < 0 or cu_seqlens[N] > seq_len */
 #define PSB_DATA_DOC_NOT_CONTIGUOUS 4 /* a non-padding id occurs in two separate runs of a row */
+#define PSB_DATA_LENS_EXCEED_SEQ 8    /* document lengths of a row add up past seq_len */
+#define PSB_DATA_BAD_POSITIONS 16     /* logical positions break the document rule */
 
 /* Human-readable message for a status code (static storage, never NULL). */
 const char* psb_status_string(psb_status status);
@@ -73,6 +75,43 @@ int32_t psb_version(void);
  */
 psb_status psb_doc_ids_from_cu_seqlens(const int32_t* cu_seqlens, int64_t n_docs, int64_t seq_len,
                                        int32_t* doc_ids_out, int32_t* status_word, void* stream);
+
+/*
+ * Document ids from per-document lengths (glm5_next.cp page,
+ * doc_ids_from_seq_lens: lengths [batch, documents] -> ids [batch, sequence];
+ * the inkling2 context_parallel page's unpack_row_layout pads such length tables
+ * with -1000).
+ *
+ *   seq_lens       device int32 [B, n_docs], contiguous.  In each row the lengths
+ *                  up to the first negative entry are documents (0 allowed: the
+ *                  document takes an id and covers nothing).
+ *   seq_len        row length S of the output.
+ *   padding_value  id of positions no document covers (the page's default: -1000).
+ *   doc_ids_out    device int32 [B, seq_len], contiguous: the j-th document of a row
+ *                  covers the next seq_lens[b, j] positions with id j + 1.
+ *   status_word    device int32 or NULL: PSB_DATA_LENS_EXCEED_SEQ is OR-ed in when a
+ *                  row's lengths add up past seq_len (the output is then unspecified).
+ * n_docs > 4096 returns PSB_ERR_UNSUPPORTED; B > 65535 PSB_ERR_SHAPE.
+ */
+psb_status psb_doc_ids_from_seq_lens(const int32_t* seq_lens, int64_t B, int64_t n_docs, int64_t seq_len,
+                                     int32_t padding_value, int32_t* doc_ids_out, int32_t* status_word,
+                                     void* stream);
+
+/*
+ * Checks logical positions against the document rule (inkling2 context_parallel
+ * page, validate_document_positions): inside a document positions grow by one, a
+ * new document starts at 0, a gap never resumes an earlier document, and the first
+ * kept token of a row may carry any non-negative offset (a shard can start inside a
+ * document).  For the kept tokens of each row in order: the first >= 0; one right
+ * after a kept token equals the previous + 1 or 0; one after dropped tokens equals 0.
+ *
+ *   keep         device uint8 [B, S] (0 = dropped), contiguous.
+ *   positions    device int32 [B, S], contiguous.
+ *   status_word  device int32, required: PSB_DATA_BAD_POSITIONS is OR-ed in when a
+ *                row breaks the rule.  Diagnostic, not on the hot path.
+ */
+psb_status psb_validate_document_positions(const uint8_t* keep, const int32_t* positions, int64_t B, int64_t S,
+                                           int32_t* status_word, void* stream);
 
 /*
  * Boundaries of the maximal runs of equal document ids of one row, padding runs

@@ -25,6 +25,8 @@ PAD_DOC_ID = -1000
 DATA_CU_NOT_MONOTONE = 1
 DATA_CU_OUT_OF_RANGE = 2
 DATA_DOC_NOT_CONTIGUOUS = 4
+DATA_LENS_EXCEED_SEQ = 8
+DATA_BAD_POSITIONS = 16
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -37,6 +39,8 @@ SIGNATURES = {
     "psb_doc_ids_from_cu_seqlens": (_c_i32, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "psb_segment_cu_seqlens": (_c_i32, [_vp, _c_i64, _vp, _c_i64, _vp, _vp]),
     "psb_validate_doc_ids": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "psb_doc_ids_from_seq_lens": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _vp, _vp]),
+    "psb_validate_document_positions": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
     "psb_blockdiag_attn_fwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
     "psb_blockdiag_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, ctypes.c_size_t,
@@ -284,3 +288,40 @@ def blockdiag_attn_bwd(q, k, v, out, dout, lse, doc_ids, workspace, seq_start: i
         int(seq_start), sc, 1 if enable_gqa else 0, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
         None, _vp(_stream(q))), "blockdiag_attn_bwd_planned")
     return dq, dk, dv
+
+
+def doc_ids_from_seq_lens(seq_lens: torch.Tensor, seq_len: int, padding_value: int = PAD_DOC_ID,
+                          validate: bool = False) -> torch.Tensor:
+    """Document ids ``[batch, seq_len]`` (int32) from lengths ``[batch, documents]``.
+
+    In each row the lengths up to the first negative entry are documents; the j-th
+    covers the next ``seq_lens[b, j]`` positions with id j + 1, the rest of the row
+    gets ``padding_value``.  ``validate=True`` synchronizes and raises
+    ``ValueError`` when a row's lengths add up past ``seq_len``.
+    """
+    _need_gpu(seq_lens)
+    lens = seq_lens if seq_lens.dim() == 2 else seq_lens.reshape(1, -1)
+    lens = (lens if lens.dtype == torch.int32 else lens.to(torch.int32)).contiguous()
+    B, n = lens.shape
+    out = torch.empty((B, int(seq_len)), dtype=torch.int32, device=lens.device)
+    status = torch.zeros(1, dtype=torch.int32, device=lens.device) if validate else None
+    _check(load().psb_doc_ids_from_seq_lens(_ptr(lens), B, n, int(seq_len), int(padding_value), _ptr(out),
+                                            _ptr(status), _vp(_stream(lens))), "doc_ids_from_seq_lens")
+    if validate and int(status.item()) != 0:
+        raise ValueError(f"document lengths exceed seq_len (status bits {int(status.item())})")
+    return out
+
+
+def validate_document_positions(keep: torch.Tensor, positions: torch.Tensor) -> None:
+    """Raises ``ValueError`` unless every row's logical positions follow the document
+    rule (synchronizes once)."""
+    _need_gpu(keep, positions)
+    if keep.shape != positions.shape or keep.dim() != 2:
+        raise ValueError("keep and positions must both be [batch, sequence]")
+    k = keep.to(torch.uint8).contiguous()
+    p = (positions if positions.dtype == torch.int32 else positions.to(torch.int32)).contiguous()
+    status = torch.zeros(1, dtype=torch.int32, device=keep.device)
+    _check(load().psb_validate_document_positions(_ptr(k), _ptr(p), k.shape[0], k.shape[1], _ptr(status),
+                                                  _vp(_stream(k))), "validate_document_positions")
+    if int(status.item()) != 0:
+        raise ValueError("positions break the document rule")

@@ -151,6 +151,97 @@ __global__ void __launch_bounds__(256) contiguity_kernel(const int32_t* __restri
   if (__any(dup) && lane == 0) atomicOr(status, PSB_DATA_DOC_NOT_CONTIGUOUS);
 }
 
+// ---- doc_ids_from_seq_lens ---------------------------------------------------------
+// Grid (position chunks, rows).  Each workgroup copies its row's length table into
+// LDS (at most kCuLds entries), turns it into boundaries with a workgroup scan (a
+// negative entry ends the list), then maps its positions like doc_ids_kernel.
+constexpr int kLensThreads = 256;
+
+__global__ void __launch_bounds__(kLensThreads) doc_ids_lens_kernel(const int32_t* __restrict__ lens,
+                                                                     int32_t n_docs, int32_t seq_len,
+                                                                     int32_t pad_value, int32_t* __restrict__ ids,
+                                                                     int32_t* __restrict__ status) {
+  __shared__ int32_t scu[kCuLds + 1];
+  __shared__ int32_t wtot[kLensThreads / kWave];
+  __shared__ int32_t s_n;
+  const int32_t b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int32_t* row = lens + (int64_t)b * n_docs;
+  if (tid == 0) s_n = n_docs;
+  __syncthreads();
+  // documents end at the first negative entry
+  constexpr int kPer = kCuLds / kLensThreads;
+  int32_t v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int32_t i = tid * kPer + j;
+    v[j] = (i < n_docs) ? row[i] : -1;
+    if (i < n_docs && v[j] < 0) atomicMin(&s_n, i);
+  }
+  __syncthreads();
+  const int32_t n = s_n;
+  int64_t loc = 0;  // sums of up to 4096 int32 lengths fit in int64; capped below
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) loc += (tid * kPer + j < n) ? v[j] : 0;
+  int64_t inc = loc;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t t = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += t;
+  }
+  if (lane == kWave - 1) wtot[wv] = (int32_t)min(inc, (int64_t)INT32_MAX);
+  __syncthreads();
+  int64_t base = 0;
+  for (int w = 0; w < wv; ++w) base += wtot[w];
+  int64_t run = base + inc - loc;  // exclusive prefix of this thread's first entry
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int32_t i = tid * kPer + j;
+    if (i < n) {
+      scu[i] = (int32_t)min(run, (int64_t)INT32_MAX);
+      run += v[j];
+    }
+    if (i == n - 1) scu[n] = (int32_t)min(run, (int64_t)INT32_MAX);
+  }
+  if (tid == 0 && n == 0) scu[0] = 0;
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0 && status != nullptr && scu[n] > seq_len) atomicOr(status, PSB_DATA_LENS_EXCEED_SEQ);
+  const int32_t p = blockIdx.x * kLensThreads + tid;
+  if (p >= seq_len) return;
+  const int32_t i = last_le(scu, n + 1, p);
+  ids[(int64_t)b * seq_len + p] = (i >= 0 && i < n) ? i + 1 : pad_value;
+}
+
+// ---- document positions ------------------------------------------------------------
+// One workgroup per row.  Pass 1 finds the first kept token; pass 2 checks every kept
+// token against its predecessor (the rule of document_positions_valid in the oracle:
+// first kept >= 0; after a kept token previous + 1 or 0; after a dropped one 0).
+constexpr int kPosThreads = 1024;
+
+__global__ void __launch_bounds__(kPosThreads) positions_kernel(const uint8_t* __restrict__ keep,
+                                                                 const int32_t* __restrict__ pos, int32_t S,
+                                                                 int32_t* __restrict__ status) {
+  __shared__ int32_t s_first;
+  const int32_t b = blockIdx.x;
+  const uint8_t* krow = keep + (int64_t)b * S;
+  const int32_t* prow = pos + (int64_t)b * S;
+  if (threadIdx.x == 0) s_first = INT32_MAX;
+  __syncthreads();
+  for (int32_t p = threadIdx.x; p < S; p += kPosThreads)
+    if (krow[p]) { atomicMin(&s_first, p); break; }
+  __syncthreads();
+  const int32_t first = s_first;
+  bool bad = false;
+  for (int32_t p = threadIdx.x; p < S; p += kPosThreads) {
+    if (!krow[p]) continue;
+    const int32_t x = prow[p];
+    if (p == first) bad |= x < 0;
+    else if (krow[p - 1]) bad |= !(x == 0 || x == prow[p - 1] + 1);
+    else bad |= x != 0;
+  }
+  if (__any(bad) && (threadIdx.x % kWave) == 0) atomicOr(status, PSB_DATA_BAD_POSITIONS);
+}
+
 }  // namespace
 }  // namespace psb
 
@@ -193,6 +284,33 @@ PSB_API psb_status psb_validate_doc_ids(const int32_t* doc_ids, int64_t B, int64
   if (blocks >= INT32_MAX) return PSB_ERR_SHAPE;
   contiguity_kernel<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(doc_ids, B, (int32_t)S,
                                                                                   row_stride, status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_doc_ids_from_seq_lens(const int32_t* seq_lens, int64_t B, int64_t n_docs, int64_t seq_len,
+                                             int32_t padding_value, int32_t* doc_ids_out, int32_t* status_word,
+                                             void* stream) {
+  if (B < 0 || n_docs < 0 || seq_len < 0) return PSB_ERR_INVALID_ARG;
+  if (B == 0 || seq_len == 0) return PSB_OK;
+  if (doc_ids_out == nullptr || (n_docs > 0 && seq_lens == nullptr)) return PSB_ERR_INVALID_ARG;
+  if (seq_len >= INT32_MAX || B > 65535) return PSB_ERR_SHAPE;
+  if (n_docs > kCuLds) return PSB_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)ceil_div(seq_len, kLensThreads), (unsigned)B);
+  doc_ids_lens_kernel<<<grid, dim3(kLensThreads), 0, as_stream(stream)>>>(
+      seq_lens, (int32_t)n_docs, (int32_t)seq_len, padding_value, doc_ids_out, status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_validate_document_positions(const uint8_t* keep, const int32_t* positions, int64_t B,
+                                                   int64_t S, int32_t* status_word, void* stream) {
+  if (B < 0 || S < 0 || status_word == nullptr) return PSB_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return PSB_OK;
+  if (keep == nullptr || positions == nullptr) return PSB_ERR_INVALID_ARG;
+  if (S >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
+  positions_kernel<<<dim3((unsigned)B), dim3(kPosThreads), 0, as_stream(stream)>>>(keep, positions, (int32_t)S,
+                                                                                 status_word);
   PSB_LAUNCH_CHECK();
   return PSB_OK;
 }

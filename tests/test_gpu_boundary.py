@@ -108,3 +108,58 @@ def test_contiguity_validation(psb):
     bad2 = _dev([[4, -1000, 4]])
     with pytest.raises(ValueError):
         psb.validate_doc_ids(bad2)
+
+
+# ---- boundary variants: lengths table, document positions ------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_doc_ids_from_seq_lens(psb, seed):
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.integers(1, 5))
+    n = int(rng.choice([1, 5, 40, 700]))
+    S = int(rng.integers(1, 5000))
+    lens = rng.integers(0, max(2, 2 * S // max(n, 1)), size=(B, n)).astype(np.int32)
+    for b in range(B):  # some rows end early with the -1000 sentinel; keep sums <= S
+        cut = int(rng.integers(0, n + 1))
+        lens[b, cut:] = -1000
+        c = np.cumsum(np.maximum(lens[b], 0))
+        lens[b, c > S] = -1000
+    say("seq_lens ids seed", seed, "B", B, "n", n, "S", S)
+    got = psb.doc_ids_from_seq_lens(_dev(lens), S, validate=True)
+    assert np.array_equal(got.cpu().numpy(), oracle.doc_ids_from_seq_lens(lens, S))
+
+
+def test_doc_ids_from_seq_lens_overflow_sets_status(psb):
+    with pytest.raises(ValueError):
+        psb.doc_ids_from_seq_lens(_dev(np.asarray([[5, 5]], dtype=np.int32)), 7, validate=True)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_document_positions(psb, seed):
+    rng = np.random.default_rng(400 + seed)
+    B, S = int(rng.integers(1, 4)), int(rng.integers(1, 3000))
+    keep = np.zeros((B, S), dtype=bool)
+    pos = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        p, first = int(rng.integers(0, 4)), True
+        while p < S:
+            n = int(rng.integers(1, 300))
+            off = int(rng.integers(0, 50)) if first else 0
+            m = min(n, S - p)
+            keep[b, p:p + m] = True
+            pos[b, p:p + m] = off + np.arange(m)
+            p += n + int(rng.integers(0, 3))
+            first = False
+        if seed % 2 == 1:  # break one row at one kept position
+            kept = np.nonzero(keep[b])[0]
+            if kept.size > 1:
+                i = int(rng.choice(kept[1:]))
+                pos[b, i] = pos[b, i - 1] + 2 if keep[b, i - 1] else 5
+    say("positions seed", seed, "B", B, "S", S)
+    want = bool(np.all(oracle.document_positions_valid(keep, pos)))
+    ok = True
+    try:
+        psb.validate_document_positions(torch.as_tensor(keep).cuda(), torch.as_tensor(pos).cuda())
+    except ValueError:
+        ok = False
+    assert ok == want
