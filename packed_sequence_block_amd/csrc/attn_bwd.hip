@@ -34,6 +34,12 @@ namespace psb {
 namespace {
 
 constexpr int kBwdWaves = 4;
+// LDS row padding (elements).  Each tile is read both row-wise (ds_read_b128: no bank
+// conflicts for a pitch of 16 bytes mod 32) and through transposing reads (no
+// conflicts for 64 bytes mod 256); no pitch serves both.  Measured: dq keeps the
+// b128-friendly pitch, dk/dv reads Q / dO best at D + 16.
+constexpr int DQ_KPAD = 8;
+constexpr int DKV_QPAD = 16;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 constexpr int kKeysPerWave = 32;                       // dkdv: keys per wave
 constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgroup
@@ -86,11 +92,12 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
-  constexpr int KROW = D + 8;
+  constexpr int KROW = D + DQ_KPAD;                       // padded K / V tile row
+  constexpr int KCH = KROW / 8;                           // 16-byte slots per row
   constexpr int KSTAGE = kKeysPerTile * KROW;
-  constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;
+  constexpr int KSEGS = kKeysPerTile * KCH / 64;
   constexpr int KSEG_ITERS = (KSEGS + kBwdWaves - 1) / kBwdWaves;
-  static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "tile segments");
+  static_assert(KSEGS * 64 == kKeysPerTile * KCH && KSTAGE * 2 == KSEGS * 1024, "tile segments");
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[KSTAGE];
@@ -108,7 +115,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 #pragma unroll
   for (int j = 0; j < KSEG_ITERS; ++j) {
     const int slot = (j * kBwdWaves + wv) * 64 + lane;
-    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
+    const int row = slot / KCH, ch = slot % KCH;
     koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
   }
   const int k_rd = lr * KROW + 8 * h;  // row-major operand read base (A = K or V rows)
@@ -293,8 +300,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
-  constexpr int QROW = D + 8;                                 // padded Q / dO tile row
-  constexpr int QSLOTS = kRowsPerStep * (NCH + 1);            // 16-byte slots of a tile
+  constexpr int QROW = D + DKV_QPAD;                          // padded Q / dO tile row
+  constexpr int QCH = QROW / 8;                               // 16-byte slots per row
+  constexpr int QSLOTS = kRowsPerStep * QCH;                  // 16-byte slots of a tile
   constexpr int QSEGS = (QSLOTS + 63) / 64;                   // 1 KiB wave-wide loads
   constexpr int QSEG_ITERS = (QSEGS + kBwdWaves - 1) / kBwdWaves;
   constexpr int QSTAGE = QSEGS * 512;                         // elements (last segment partly spare)
@@ -319,7 +327,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int j = 0; j < QSEG_ITERS; ++j) {
     const int slot = (j * kBwdWaves + wv) * 64 + lane;
-    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
+    const int row = slot / QCH, ch = slot % QCH;
     qoff[j] = (slot < QSLOTS && ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
   }
   const int a_rd = lr * QROW + 8 * h;  // A = Q / dO rows (lane = row)
