@@ -165,3 +165,38 @@ def test_autograd_function(psb):
     check_grad(qd.grad, rq, "autograd dq")
     check_grad(kd.grad, rk, "autograd dk")
     check_grad(vd.grad, rv, "autograd dv")
+
+
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_full_size_one_document(psb, c):
+    # the full-size training path (all rows, all heads, the bench's configuration), checked
+    # on one document: its rows' dq depend only on those rows, and its keys' dk / dv only
+    # on the rows of the same document, so the oracle on that document alone gives them
+    lay = make_layout(c)
+    q, k, v = make_qkv(lay)
+    ids = oracle_doc_ids(lay)
+    g = torch.Generator().manual_seed(50 + c)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    dev = "cuda"
+    say("bwd full size", lay.name)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    idd = torch.as_tensor(ids, dtype=torch.int32).to(dev)
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(qd, kd, vd, idd, lay.seq_start, None, lay.enable_gqa)
+    dq, dk, dv = psb.blockdiag_attn_bwd(qd, kd, vd, out, dout.to(dev), lse, idd, ws, lay.seq_start, None,
+                                        lay.enable_gqa)
+    torch.cuda.synchronize()
+    # a document that lies inside the query shard, of moderate length
+    b = 0
+    cu = lay.cu_seqlens(b)
+    lo_q, hi_q = lay.seq_start, lay.seq_start + lay.L
+    cands = [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)
+             if cu[i] >= lo_q and cu[i + 1] <= hi_q and 64 <= cu[i + 1] - cu[i] <= 1500]
+    assert cands, "no document of moderate length inside the shard"
+    d0, d1 = cands[len(cands) // 2]
+    r0, r1 = d0 - lay.seq_start, d1 - lay.seq_start
+    sub = np.asarray(ids[b:b + 1])
+    rq, rk, rv = oracle.blockdiag_attn_bwd(q[b:b + 1, :, r0:r1], k[b:b + 1], v[b:b + 1], dout[b:b + 1, :, r0:r1],
+                                           sub, d0, None, lay.enable_gqa)
+    check_grad(dq[b:b + 1, :, r0:r1].cpu(), rq, f"{lay.name} dq")
+    check_grad(dk[b:b + 1, :, d0:d1].cpu(), rk[:, :, d0:d1], f"{lay.name} dk")
+    check_grad(dv[b:b + 1, :, d0:d1].cpu(), rv[:, :, d0:d1], f"{lay.name} dv")
