@@ -21,7 +21,7 @@ Sources followed (cite by page title and section):
   output ``[B, Hq, L, D]`` for the local rows), ``BlockdiagCpModelState``
   (``packed_cu_seqlens`` has shape ``[num_documents + 1]``).
 
-Readings where the pages are silent (each is listed in the design doc too):
+Readings where the pages are silent:
 
 * padding document id is -1000 (the sentinel of ``doc_ids_from_seq_lens`` and
   of the inkling2 ``unpack_row_layout`` lengths); 0 is an ordinary id;
