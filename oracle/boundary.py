@@ -120,3 +120,48 @@ def document_positions_valid(keep, positions) -> np.ndarray:
                 break
             seen = True
     return ok
+
+
+def unpack_row_layout(seq_lens, seq_lens_padded, seq_len: int):
+    """Packed length tables -> ``(padding_mask [B, seq_len] bool, position_ids [B, seq_len] int32)``.
+
+    inkling2 ``context_parallel`` page, ``unpack_row_layout``: the packer hands over
+    real and padded lengths ``[batch, documents]``, both padded with -1000, and
+    padding comes from those lengths alone, never from token ids; the result is a
+    boolean padding mask and integer positions ``[batch, sequence]``.  Readings:
+      * a row's documents are the entries before the first negative padded length;
+        document j takes the next ``seq_lens_padded[b, j]`` positions of the row;
+      * of those, the first ``seq_lens[b, j]`` are real tokens with positions
+        0, 1, ... inside the document; the rest of the block is padding;
+      * positions past the last document are padding;
+      * padding positions get ``padding_mask`` True (the blockdiag_cp page's
+        ``make_cp_blockdiag_batch_and_ctx`` convention, True == pad) and position 0;
+      * ``0 <= seq_lens[b, j] <= seq_lens_padded[b, j]`` for every document and
+        padded lengths adding up to at most ``seq_len``; anything else raises
+        ``ValueError``.
+    """
+    real = np.asarray(seq_lens, dtype=np.int64)
+    padded = np.asarray(seq_lens_padded, dtype=np.int64)
+    if real.ndim != 2 or real.shape != padded.shape:
+        raise ValueError("seq_lens and seq_lens_padded must both be [batch, documents]")
+    if seq_len < 0:
+        raise ValueError("negative seq_len")
+    B, N = real.shape
+    mask = np.ones((B, seq_len), dtype=bool)
+    pos = np.zeros((B, seq_len), dtype=np.int32)
+    for b in range(B):
+        start = 0
+        for j in range(N):
+            n_pad = int(padded[b, j])
+            if n_pad < 0:
+                break
+            n_real = int(real[b, j])
+            if n_real < 0 or n_real > n_pad:
+                raise ValueError(f"row {b} document {j}: real length {n_real} outside [0, {n_pad}]")
+            if start + n_pad > seq_len:
+                raise ValueError(f"row {b}: padded lengths exceed seq_len")
+            for t in range(n_real):
+                mask[b, start + t] = False
+                pos[b, start + t] = t
+            start += n_pad
+    return mask, pos

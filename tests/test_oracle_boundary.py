@@ -149,3 +149,96 @@ def test_document_positions_constructed_and_broken(seed):
         # neither 0 nor previous + 1 (after a kept token), not 0 after a gap
         bad[i] = bad[i - 1] + 2 if keep[i - 1] else 5
         assert oracle.document_positions_valid(keep[None], bad[None]).tolist() == [False]
+
+
+# ---- row layout from length tables (inkling2 context_parallel page, unpack_row_layout) ----
+
+def test_unpack_row_layout_hand_example():
+    # row 0: a 3-token document padded to 4, a 1-token document padded to 2, table end;
+    # row 1: an empty document padded to 1, then 2 real of 2
+    real = np.asarray([[3, 1, -1000], [0, 2, -1000]])
+    padded = np.asarray([[4, 2, -1000], [1, 2, -1000]])
+    mask, pos = oracle.unpack_row_layout(real, padded, 8)
+    assert mask.dtype == bool and pos.dtype == np.int32 and mask.shape == pos.shape == (2, 8)
+    np.testing.assert_array_equal(mask[0], [0, 0, 0, 1, 0, 1, 1, 1])
+    np.testing.assert_array_equal(pos[0], [0, 1, 2, 0, 0, 0, 0, 0])
+    np.testing.assert_array_equal(mask[1], [1, 0, 0, 1, 1, 1, 1, 1])
+    np.testing.assert_array_equal(pos[1], [0, 0, 1, 0, 0, 0, 0, 0])
+
+
+def _random_tables(rng, B, N, S):
+    real = np.full((B, N), -1000, dtype=np.int64)
+    padded = np.full((B, N), -1000, dtype=np.int64)
+    for b in range(B):
+        left = S
+        for j in range(int(rng.integers(0, N + 1))):
+            n_pad = int(rng.integers(0, 12))
+            if n_pad > left:
+                break
+            real[b, j], padded[b, j] = int(rng.integers(0, n_pad + 1)), n_pad
+            left -= n_pad
+    return real, padded
+
+
+def _brute_unpack(real, padded, S):
+    # per row: concatenate, document by document, "real tokens" then "padding" blocks
+    B = real.shape[0]
+    mask = np.ones((B, S), dtype=bool)
+    pos = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        n = int(np.argmax(padded[b] < 0)) if (padded[b] < 0).any() else padded.shape[1]
+        m_parts = [np.concatenate([np.zeros(r, bool), np.ones(q - r, bool)]) for r, q in zip(real[b, :n], padded[b, :n])]
+        p_parts = [np.concatenate([np.arange(r), np.zeros(q - r, np.int64)]) for r, q in zip(real[b, :n], padded[b, :n])]
+        body_m = np.concatenate(m_parts) if m_parts else np.zeros(0, bool)
+        body_p = np.concatenate(p_parts) if p_parts else np.zeros(0, np.int64)
+        mask[b, :body_m.size] = body_m
+        pos[b, :body_p.size] = body_p
+    return mask, pos
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_unpack_row_layout_random_against_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    S = int(rng.integers(0, 60))
+    real, padded = _random_tables(rng, 3, 7, S)
+    mask, pos = oracle.unpack_row_layout(real, padded, S)
+    bm, bp = _brute_unpack(real, padded, S)
+    np.testing.assert_array_equal(mask, bm)
+    np.testing.assert_array_equal(pos, bp)
+    # invariants: as many real tokens as the real lengths say, and the kept tokens
+    # follow the document rule (each document restarts at 0 after its padding)
+    for b in range(3):
+        n = int(np.argmax(padded[b] < 0)) if (padded[b] < 0).any() else padded.shape[1]
+        assert int((~mask[b]).sum()) == int(real[b, :n].sum())
+    assert oracle.document_positions_valid(~mask, pos).all()
+
+
+def test_unpack_row_layout_without_padding_matches_doc_ids():
+    # equal tables: no padding inside the documents; the kept tokens are exactly the
+    # positions doc_ids_from_seq_lens covers, and a token's position is its distance
+    # from the first position that carries its id
+    lens = np.asarray([[5, 0, 3, 4, -1000], [2, 2, 2, 2, 2]])
+    mask, pos = oracle.unpack_row_layout(lens, lens, 12)
+    ids = oracle.doc_ids_from_seq_lens(lens, 12)
+    np.testing.assert_array_equal(mask, ids == PAD_DOC_ID)
+    for b in range(2):
+        for p in range(12):
+            if ids[b, p] != PAD_DOC_ID:
+                assert pos[b, p] == p - int(np.argmax(ids[b] == ids[b, p]))
+
+
+@pytest.mark.parametrize("real,padded,S", [
+    ([[3, 2]], [[2, 2]], 8),          # more real tokens than the padded block
+    ([[-1, 2]], [[2, 2]], 8),         # real table ends before the padded one
+    ([[3, 3]], [[4, 5]], 8),          # padded lengths exceed seq_len
+])
+def test_unpack_row_layout_invalid_raises(real, padded, S):
+    with pytest.raises(ValueError):
+        oracle.unpack_row_layout(np.asarray(real), np.asarray(padded), S)
+
+
+def test_unpack_row_layout_empty():
+    mask, pos = oracle.unpack_row_layout(np.zeros((2, 0), np.int64), np.zeros((2, 0), np.int64), 3)
+    assert mask.all() and (pos == 0).all()
+    mask, pos = oracle.unpack_row_layout(np.asarray([[0]]), np.asarray([[0]]), 0)
+    assert mask.shape == (1, 0)
