@@ -50,6 +50,7 @@ typedef int32_t psb_status;
 #define PSB_DATA_DOC_NOT_CONTIGUOUS 4 /* a non-padding id occurs in two separate runs of a row */
 #define PSB_DATA_LENS_EXCEED_SEQ 8    /* document lengths of a row add up past seq_len */
 #define PSB_DATA_BAD_POSITIONS 16     /* logical positions break the document rule */
+#define PSB_DATA_BAD_LENGTHS 32       /* a real document length is negative or above its padded length */
 
 /* Human-readable message for a status code (static storage, never NULL). */
 const char* psb_status_string(psb_status status);
@@ -96,6 +97,30 @@ psb_status psb_doc_ids_from_cu_seqlens(const int32_t* cu_seqlens, int64_t n_docs
 psb_status psb_doc_ids_from_seq_lens(const int32_t* seq_lens, int64_t B, int64_t n_docs, int64_t seq_len,
                                      int32_t padding_value, int32_t* doc_ids_out, int32_t* status_word,
                                      void* stream);
+
+/*
+ * Padding mask and document positions of packed rows from their length tables
+ * (inkling2 context_parallel page, unpack_row_layout: the packer's real and padded
+ * lengths [batch, documents], padded with -1000, decide padding; token ids never do).
+ *
+ *   seq_lens, seq_lens_padded  device int32 [B, n_docs], contiguous.  A row's
+ *                    documents are the entries before its first negative padded
+ *                    length; document j takes the next seq_lens_padded[b, j]
+ *                    positions, of which the first seq_lens[b, j] are real tokens.
+ *   padding_mask_out device uint8 [B, seq_len], contiguous: 0 for a real token, 1 for
+ *                    padding (inside a document's padded block or past the last one).
+ *   position_ids_out device int32 [B, seq_len], contiguous: a real token's offset in
+ *                    its document (0, 1, ...); 0 at padding.
+ *   status_word      device int32 or NULL: PSB_DATA_BAD_LENGTHS is OR-ed in when some
+ *                    0 <= seq_lens[b, j] <= seq_lens_padded[b, j] fails,
+ *                    PSB_DATA_LENS_EXCEED_SEQ when a row's padded lengths add up past
+ *                    seq_len (the outputs are then unspecified).
+ * The caller owns every buffer.  n_docs > 4096 returns PSB_ERR_UNSUPPORTED; B > 65535
+ * PSB_ERR_SHAPE; B == 0 or seq_len == 0 enqueues nothing.
+ */
+psb_status psb_unpack_row_layout(const int32_t* seq_lens, const int32_t* seq_lens_padded, int64_t B, int64_t n_docs,
+                                 int64_t seq_len, uint8_t* padding_mask_out, int32_t* position_ids_out,
+                                 int32_t* status_word, void* stream);
 
 /*
  * Checks logical positions against the document rule (inkling2 context_parallel

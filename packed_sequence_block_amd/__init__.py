@@ -14,12 +14,14 @@ Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
 
 from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd, blockdiag_attn_fwd_lse,
                    bwd_workspace_size, doc_ids_from_cu_seqlens, doc_ids_from_seq_lens, load,
-                   segment_cu_seqlens, status_string, validate_doc_ids, validate_document_positions,
+                   segment_cu_seqlens, status_string, unpack_row_layout, unpack_row_layout_batch, validate_doc_ids,
+                   validate_document_positions,
                    workspace_size)
 
 from .autograd import blockdiag_attention
 
 __all__ = ["blockdiag_attention", "PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
            "bwd_workspace_size", "doc_ids_from_cu_seqlens", "doc_ids_from_seq_lens", "load",
-           "segment_cu_seqlens", "status_string", "validate_doc_ids", "validate_document_positions",
+           "segment_cu_seqlens", "status_string", "unpack_row_layout", "unpack_row_layout_batch", "validate_doc_ids",
+           "validate_document_positions",
            "workspace_size"]

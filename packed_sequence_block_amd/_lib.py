@@ -27,6 +27,7 @@ DATA_CU_OUT_OF_RANGE = 2
 DATA_DOC_NOT_CONTIGUOUS = 4
 DATA_LENS_EXCEED_SEQ = 8
 DATA_BAD_POSITIONS = 16
+DATA_BAD_LENGTHS = 32
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -41,6 +42,7 @@ SIGNATURES = {
     "psb_validate_doc_ids": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
     "psb_doc_ids_from_seq_lens": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _vp, _vp]),
     "psb_validate_document_positions": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
+    "psb_unpack_row_layout": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
     "psb_blockdiag_attn_fwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
     "psb_blockdiag_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, ctypes.c_size_t,
@@ -310,6 +312,46 @@ def doc_ids_from_seq_lens(seq_lens: torch.Tensor, seq_len: int, padding_value: i
     if validate and int(status.item()) != 0:
         raise ValueError(f"document lengths exceed seq_len (status bits {int(status.item())})")
     return out
+
+
+def unpack_row_layout(seq_lens: torch.Tensor, seq_lens_padded: torch.Tensor, seq_len: int,
+                      validate: bool = False):
+    """``(padding_mask [B, seq_len] bool, position_ids [B, seq_len] int32)`` from the
+    packer's real / padded length tables ``[batch, documents]`` (-1000-padded).
+
+    Document j of a row takes the next ``seq_lens_padded[b, j]`` positions; its first
+    ``seq_lens[b, j]`` are real tokens at positions 0, 1, ...; every other position is
+    padding (mask True, position 0).  ``validate=True`` synchronizes and raises
+    ``ValueError`` for a real length outside ``[0, padded]`` or padded lengths that add
+    up past ``seq_len``.
+    """
+    _need_gpu(seq_lens, seq_lens_padded)
+    if seq_lens.shape != seq_lens_padded.shape:
+        raise ValueError("seq_lens and seq_lens_padded must have one shape")
+    tabs = []
+    for t in (seq_lens, seq_lens_padded):
+        t = t if t.dim() == 2 else t.reshape(1, -1)
+        tabs.append((t if t.dtype == torch.int32 else t.to(torch.int32)).contiguous())
+    B, n = tabs[0].shape
+    dev = tabs[0].device
+    mask = torch.empty((B, int(seq_len)), dtype=torch.bool, device=dev)
+    pos = torch.empty((B, int(seq_len)), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev) if validate else None
+    _check(load().psb_unpack_row_layout(_ptr(tabs[0]), _ptr(tabs[1]), B, n, int(seq_len), _ptr(mask), _ptr(pos),
+                                        _ptr(status), _vp(_stream(tabs[0]))), "unpack_row_layout")
+    if validate and int(status.item()) != 0:
+        raise ValueError(f"bad length tables (status bits {int(status.item())})")
+    return mask, pos
+
+
+def unpack_row_layout_batch(batch: dict, validate: bool = False) -> None:
+    """In place on a batch mapping: replaces ``seq_lens`` / ``seq_lens_padded`` with a
+    boolean ``padding_mask`` and ``position_ids`` of the shape of ``input_ids``; token
+    ids and labels are left as they are."""
+    S = batch["input_ids"].shape[-1]
+    mask, pos = unpack_row_layout(batch.pop("seq_lens"), batch.pop("seq_lens_padded"), S, validate)
+    batch["padding_mask"] = mask
+    batch["position_ids"] = pos
 
 
 def validate_document_positions(keep: torch.Tensor, positions: torch.Tensor) -> None:

@@ -151,35 +151,30 @@ __global__ void __launch_bounds__(256) contiguity_kernel(const int32_t* __restri
   if (__any(dup) && lane == 0) atomicOr(status, PSB_DATA_DOC_NOT_CONTIGUOUS);
 }
 
-// ---- doc_ids_from_seq_lens ---------------------------------------------------------
+// ---- doc_ids_from_seq_lens / unpack_row_layout -------------------------------------
 // Grid (position chunks, rows).  Each workgroup copies its row's length table into
 // LDS (at most kCuLds entries), turns it into boundaries with a workgroup scan (a
 // negative entry ends the list), then maps its positions like doc_ids_kernel.
 constexpr int kLensThreads = 256;
 
-__global__ void __launch_bounds__(kLensThreads) doc_ids_lens_kernel(const int32_t* __restrict__ lens,
-                                                                     int32_t n_docs, int32_t seq_len,
-                                                                     int32_t pad_value, int32_t* __restrict__ ids,
-                                                                     int32_t* __restrict__ status) {
-  __shared__ int32_t scu[kCuLds + 1];
-  __shared__ int32_t wtot[kLensThreads / kWave];
-  __shared__ int32_t s_n;
-  const int32_t b = blockIdx.y;
+// Boundaries of one row's length table: scu[0..n] = 0, l0, l0 + l1, ... (capped at
+// INT32_MAX), where n is the index of the first negative entry (n_docs if none).
+// Every thread of the workgroup must call it; returns n.
+__device__ int32_t lens_to_bounds(const int32_t* __restrict__ row, int32_t n_docs, int32_t* scu,
+                                  int32_t* wtot, int32_t* s_n) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-  const int32_t* row = lens + (int64_t)b * n_docs;
-  if (tid == 0) s_n = n_docs;
+  if (tid == 0) *s_n = n_docs;
   __syncthreads();
-  // documents end at the first negative entry
   constexpr int kPer = kCuLds / kLensThreads;
   int32_t v[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int32_t i = tid * kPer + j;
     v[j] = (i < n_docs) ? row[i] : -1;
-    if (i < n_docs && v[j] < 0) atomicMin(&s_n, i);
+    if (i < n_docs && v[j] < 0) atomicMin(s_n, i);
   }
   __syncthreads();
-  const int32_t n = s_n;
+  const int32_t n = *s_n;
   int64_t loc = 0;  // sums of up to 4096 int32 lengths fit in int64; capped below
 #pragma unroll
   for (int j = 0; j < kPer; ++j) loc += (tid * kPer + j < n) ? v[j] : 0;
@@ -205,11 +200,60 @@ __global__ void __launch_bounds__(kLensThreads) doc_ids_lens_kernel(const int32_
   }
   if (tid == 0 && n == 0) scu[0] = 0;
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0 && status != nullptr && scu[n] > seq_len) atomicOr(status, PSB_DATA_LENS_EXCEED_SEQ);
-  const int32_t p = blockIdx.x * kLensThreads + tid;
+  return n;
+}
+
+__global__ void __launch_bounds__(kLensThreads) doc_ids_lens_kernel(const int32_t* __restrict__ lens,
+                                                                     int32_t n_docs, int32_t seq_len,
+                                                                     int32_t pad_value, int32_t* __restrict__ ids,
+                                                                     int32_t* __restrict__ status) {
+  __shared__ int32_t scu[kCuLds + 1];
+  __shared__ int32_t wtot[kLensThreads / kWave];
+  __shared__ int32_t s_n;
+  const int32_t b = blockIdx.y;
+  const int32_t n = lens_to_bounds(lens + (int64_t)b * n_docs, n_docs, scu, wtot, &s_n);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && status != nullptr && scu[n] > seq_len)
+    atomicOr(status, PSB_DATA_LENS_EXCEED_SEQ);
+  const int32_t p = blockIdx.x * kLensThreads + threadIdx.x;
   if (p >= seq_len) return;
   const int32_t i = last_le(scu, n + 1, p);
   ids[(int64_t)b * seq_len + p] = (i >= 0 && i < n) ? i + 1 : pad_value;
+}
+
+// unpack_row_layout: the padded lengths place the documents (boundaries as above);
+// inside document i the first real[i] positions are tokens at positions 0, 1, ...,
+// the rest of its block and everything past the last block are padding (mask 1,
+// position 0).  Workgroup (0, b) also checks 0 <= real[i] <= padded[i].
+__global__ void __launch_bounds__(kLensThreads) unpack_kernel(const int32_t* __restrict__ real,
+                                                               const int32_t* __restrict__ padded, int32_t n_docs,
+                                                               int32_t seq_len, uint8_t* __restrict__ mask,
+                                                               int32_t* __restrict__ pos,
+                                                               int32_t* __restrict__ status) {
+  __shared__ int32_t scu[kCuLds + 1];
+  __shared__ int32_t sreal[kCuLds];
+  __shared__ int32_t wtot[kLensThreads / kWave];
+  __shared__ int32_t s_n;
+  const int32_t b = blockIdx.y;
+  const int32_t* rrow = real + (int64_t)b * n_docs;
+  const int32_t n = lens_to_bounds(padded + (int64_t)b * n_docs, n_docs, scu, wtot, &s_n);
+  bool bad = false;
+  for (int32_t i = threadIdx.x; i < n; i += kLensThreads) {
+    const int32_t r = rrow[i];
+    sreal[i] = r;
+    bad |= r < 0 || r > scu[i + 1] - scu[i];
+  }
+  __syncthreads();
+  if (status != nullptr && blockIdx.x == 0) {
+    if (__any(bad) && (threadIdx.x % kWave) == 0) atomicOr(status, PSB_DATA_BAD_LENGTHS);
+    if (threadIdx.x == 0 && scu[n] > seq_len) atomicOr(status, PSB_DATA_LENS_EXCEED_SEQ);
+  }
+  const int32_t p = blockIdx.x * kLensThreads + threadIdx.x;
+  if (p >= seq_len) return;
+  const int32_t i = last_le(scu, n + 1, p);
+  const int32_t off = p - (i >= 0 ? scu[i] : 0);
+  const bool tok = i >= 0 && i < n && off < sreal[i];
+  mask[(int64_t)b * seq_len + p] = tok ? 0 : 1;
+  pos[(int64_t)b * seq_len + p] = tok ? off : 0;
 }
 
 // ---- document positions ------------------------------------------------------------
@@ -311,6 +355,23 @@ PSB_API psb_status psb_validate_document_positions(const uint8_t* keep, const in
   if (S >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
   positions_kernel<<<dim3((unsigned)B), dim3(kPosThreads), 0, as_stream(stream)>>>(keep, positions, (int32_t)S,
                                                                                  status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_unpack_row_layout(const int32_t* seq_lens, const int32_t* seq_lens_padded, int64_t B,
+                                         int64_t n_docs, int64_t seq_len, uint8_t* padding_mask_out,
+                                         int32_t* position_ids_out, int32_t* status_word, void* stream) {
+  if (B < 0 || n_docs < 0 || seq_len < 0) return PSB_ERR_INVALID_ARG;
+  if (B == 0 || seq_len == 0) return PSB_OK;
+  if (padding_mask_out == nullptr || position_ids_out == nullptr) return PSB_ERR_INVALID_ARG;
+  if (n_docs > 0 && (seq_lens == nullptr || seq_lens_padded == nullptr)) return PSB_ERR_INVALID_ARG;
+  if (seq_len >= INT32_MAX || B > 65535) return PSB_ERR_SHAPE;
+  if (n_docs > kCuLds) return PSB_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)ceil_div(seq_len, kLensThreads), (unsigned)B);
+  unpack_kernel<<<grid, dim3(kLensThreads), 0, as_stream(stream)>>>(seq_lens, seq_lens_padded, (int32_t)n_docs,
+                                                                     (int32_t)seq_len, padding_mask_out,
+                                                                     position_ids_out, status_word);
   PSB_LAUNCH_CHECK();
   return PSB_OK;
 }

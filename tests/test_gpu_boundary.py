@@ -163,3 +163,85 @@ def test_document_positions(psb, seed):
     except ValueError:
         ok = False
     assert ok == want
+
+
+def _unpack_tables(rng, B, n, S):
+    """Real / padded length tables that fit S, -1000 after each row's last document."""
+    real = np.full((B, n), -1000, dtype=np.int32)
+    padded = np.full((B, n), -1000, dtype=np.int32)
+    for b in range(B):
+        left = S
+        for j in range(int(rng.integers(0, n + 1))):
+            q = int(rng.integers(0, max(2, 3 * S // max(n, 1))))
+            if q > left:
+                break
+            real[b, j], padded[b, j] = int(rng.integers(0, q + 1)), q
+            left -= q
+    return real, padded
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_unpack_row_layout(psb, seed):
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 5))
+    n = int(rng.choice([1, 6, 90, 1000]))
+    S = int(rng.integers(1, 6000))
+    real, padded = _unpack_tables(rng, B, n, S)
+    say("unpack seed", seed, "B", B, "n", n, "S", S)
+    mask, pos = psb.unpack_row_layout(_dev(real), _dev(padded), S, validate=True)
+    want_m, want_p = oracle.unpack_row_layout(real, padded, S)
+    assert mask.dtype == torch.bool and pos.dtype == torch.int32
+    assert np.array_equal(mask.cpu().numpy(), want_m)
+    assert np.array_equal(pos.cpu().numpy(), want_p)
+
+
+def test_unpack_row_layout_full_rows_and_many_documents(psb):
+    # tables that fill the row exactly, 4096 documents (the largest table), zero lengths
+    rng = np.random.default_rng(77)
+    n, S = 4096, 4096 * 3
+    padded = rng.integers(0, 6, size=(2, n)).astype(np.int32)
+    padded[:, -1] += S - padded.sum(axis=1).astype(np.int32)
+    assert (padded >= 0).all() and (padded.sum(axis=1) == S).all()
+    real = np.minimum(padded, rng.integers(0, 6, size=(2, n))).astype(np.int32)
+    say("unpack 4096 documents")
+    mask, pos = psb.unpack_row_layout(_dev(real), _dev(padded), S, validate=True)
+    want_m, want_p = oracle.unpack_row_layout(real, padded, S)
+    assert np.array_equal(mask.cpu().numpy(), want_m) and np.array_equal(pos.cpu().numpy(), want_p)
+    with pytest.raises(psb.PsbError):
+        psb.unpack_row_layout(_dev(np.zeros((1, n + 1), np.int32)), _dev(np.zeros((1, n + 1), np.int32)), 8)
+
+
+@pytest.mark.parametrize("real,padded,S,bits", [
+    ([[3, 2]], [[2, 2]], 8, 32),          # more real tokens than the padded block
+    ([[-1, 2]], [[2, 2]], 8, 32),         # negative real length inside the table
+    ([[3, 3]], [[4, 5]], 8, 8),           # padded lengths exceed seq_len
+])
+def test_unpack_row_layout_bad_tables_set_status(psb, real, padded, S, bits):
+    lib = psb.load()
+    r, q = _dev(np.asarray(real, np.int32)), _dev(np.asarray(padded, np.int32))
+    mask = torch.empty((1, S), dtype=torch.bool, device="cuda")
+    pos = torch.empty((1, S), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    say("unpack bad table", real, padded, S)
+    st = lib.psb_unpack_row_layout(P(r), P(q), 1, r.shape[1], S, P(mask), P(pos), P(status),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and int(status.item()) == bits
+    with pytest.raises(ValueError):
+        psb.unpack_row_layout(r, q, S, validate=True)
+
+
+def test_unpack_then_positions_rule(psb):
+    # the unpacked layout passes the document rule with keep = not padding
+    rng = np.random.default_rng(5)
+    real, padded = _unpack_tables(rng, 3, 50, 3000)
+    mask, pos = psb.unpack_row_layout(_dev(real), _dev(padded), 3000)
+    say("unpack then positions")
+    psb.validate_document_positions(~mask, pos)
+    batch = {"input_ids": torch.zeros((3, 3000), dtype=torch.int64, device="cuda"),
+             "seq_lens": _dev(real), "seq_lens_padded": _dev(padded)}
+    psb.unpack_row_layout_batch(batch)
+    assert "seq_lens" not in batch and torch.equal(batch["padding_mask"], mask)
+    assert torch.equal(batch["position_ids"], pos)
