@@ -171,3 +171,27 @@ def blockdiag_attn_loop(q, k, v, doc_ids, seq_start: int = 0, scale: float | Non
                 for d in range(D):
                     out[b, h, i, d] = sum(wj * float(vn[b, g, kk, d]) for wj, kk in zip(w, keys)) / tot
     return out
+
+
+def kv_window_start(doc_ids, seq_start: int, L: int) -> np.ndarray:
+    """First key position a query shard needs, per batch row: ``[B]`` int64.
+
+    blockdiag_cp page, package overview (the ``.exchange`` layer can deliver only
+    the needed keys through a left halo instead of an all-gather) and
+    ``cp_blockdiag_sdpa`` (the local rows at ``seq_start + i``): the shard's keys
+    are its own ``[seq_start, seq_start + L)`` plus the earlier keys some local
+    query may attend to.  Taken straight from the explicit mask: the smallest
+    key column with an allowed pair for any local row, or ``seq_start`` when that
+    is smaller (or no row has a key).
+    """
+    doc_ids = torch.as_tensor(np.asarray(doc_ids)).to(torch.int64)
+    doc_ids = doc_ids.reshape(doc_ids.shape[0], -1) if doc_ids.dim() > 0 else doc_ids.reshape(1, -1)
+    out = np.full(doc_ids.shape[0], seq_start, dtype=np.int64)
+    qpos = torch.arange(seq_start, seq_start + L, dtype=torch.int64)
+    for b in range(doc_ids.shape[0]):
+        if L == 0:
+            continue
+        cols = torch.nonzero(allowed_mask(doc_ids[b], qpos).any(dim=0)).reshape(-1)
+        if cols.numel() > 0:
+            out[b] = min(seq_start, int(cols[0]))
+    return out
