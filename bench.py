@@ -109,6 +109,39 @@ def backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
             "flop_convention": "2.5 x forward useful flops"}
 
 
+def window_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
+    """The same forward with only the keys the shard needs delivered: its own
+    [seq_start, seq_start + L) plus the left halo back to the start of the document
+    crossing its first row (window start from the library's own kernel)."""
+    import torch
+    B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
+    w = int(psb.shard_kv_window_start(doc_ids, lay.seq_start, L).min().item())
+    kv_len = lay.seq_start + L - w
+    kw, vw = k[:, :, w:w + kv_len].contiguous(), v[:, :, w:w + kv_len].contiguous()
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    need = psb.workspace_size(B, Hq, Hkv, L, D)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    gqa = 1 if lay.enable_gqa else 0
+    assert lib.psb_blockdiag_attn_plan(P(doc_ids), B, Hq, Hkv, L, S, D, lay.seq_start, gqa, P(ws), need, sptr) == 0
+
+    def fwd():
+        st = lib.psb_blockdiag_attn_fwd_window_planned(P(q), P(kw), P(vw), P(doc_ids), B, Hq, Hkv, L, S, D, None,
+                                                       None, lay.seq_start, w, kv_len, float(D) ** -0.5, gqa,
+                                                       P(out), None, P(ws), need, None, sptr)
+        assert st == 0, st
+
+    for _ in range(3):
+        fwd()
+    torch.cuda.synchronize()
+    ms = timed(fwd, steps)
+    kv_bytes = 2 * B * Hkv * kv_len * D * 2
+    return {"what": "forward against the delivered key window (own keys + left halo)", "kv_start": w,
+            "keys": kv_len, "of": S, "kv_bytes": kv_bytes, "kv_bytes_whole_row": 2 * B * Hkv * S * D * 2,
+            "ms": round(ms, 5), "useful_tflops": round(lay.useful_flops() / (ms * 1e-3) / 1e12, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +256,7 @@ def main():
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
         "phase_ms": phase_ms,
     }
+    rec["kv_window"] = window_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     if not args.no_backward:
         rec["backward"] = backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     if not args.no_cpu_baseline:

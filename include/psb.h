@@ -51,6 +51,7 @@ typedef int32_t psb_status;
 #define PSB_DATA_LENS_EXCEED_SEQ 8    /* document lengths of a row add up past seq_len */
 #define PSB_DATA_BAD_POSITIONS 16     /* logical positions break the document rule */
 #define PSB_DATA_BAD_LENGTHS 32       /* a real document length is negative or above its padded length */
+#define PSB_DATA_KV_WINDOW 64         /* a query needs a key before the delivered key window */
 
 /* Human-readable message for a status code (static storage, never NULL). */
 const char* psb_status_string(psb_status status);
@@ -289,6 +290,64 @@ psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const vo
                                           int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
                                           void* dq, void* dk, void* dv, void* workspace,
                                           size_t workspace_bytes, int32_t* status_word, void* stream);
+
+/*
+ * Attention of a query shard against a delivered key WINDOW instead of the whole
+ * row (blockdiag_cp page, package overview: the exchange layer may deliver only the
+ * needed keys through a left halo, rather than all-gathering them; cp_blockdiag_sdpa:
+ * the local rows run against the delivered keys).  A shard's rows need the keys
+ * [w, seq_start + L), where w is the start of the document of its first non-padding
+ * row (psb_shard_kv_window_start); keys after seq_start + L are never needed.
+ *
+ *   k, v         device bf16 [B, Hkv, kv_len, D] (kv_strides as in the forward; NULL =
+ *                contiguous with this shape): the keys at global positions
+ *                [kv_start, kv_start + kv_len).  Requires 0 <= kv_start <= seq_start and
+ *                seq_start + L <= kv_start + kv_len <= S (else PSB_ERR_SHAPE).
+ *   doc_ids      device int32 [B, S]: the whole rows' ids, as in the forward.
+ *   lse          device fp32 [B, Hq, L] or NULL (as in psb_blockdiag_attn_fwd_lse_planned).
+ *   status_word  device int32 or NULL: PSB_DATA_KV_WINDOW is OR-ed in when some row
+ *                needs a key before kv_start; such rows then attend only to the keys
+ *                inside the window.
+ * The workspace holds a plan from psb_blockdiag_attn_plan for the same doc_ids and shape
+ * arguments (the plan does not depend on the window).  Everything else is as in
+ * psb_blockdiag_attn_fwd_planned; with kv_start = 0 and kv_len = S the results equal it.
+ */
+psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const void* k, const void* v,
+                                                 const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                                 int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                                 const int64_t* kv_strides, int64_t seq_start, int64_t kv_start,
+                                                 int64_t kv_len, float scale, int32_t enable_gqa, void* out,
+                                                 float* lse, const void* workspace, size_t workspace_bytes,
+                                                 int32_t* status_word, void* stream);
+
+/*
+ * The backward for a key window: k, v, dk, dv are device bf16 [B, Hkv, kv_len, D],
+ * contiguous, for the keys [kv_start, kv_start + kv_len); dk / dv are the gradients of
+ * those keys (the part the glm5_next.cp page's gathers route back to the ranks that own
+ * them).  Window rules and status_word as in psb_blockdiag_attn_fwd_window_planned;
+ * everything else as in psb_blockdiag_attn_bwd_planned (workspace size included).
+ */
+psb_status psb_blockdiag_attn_bwd_window_planned(const void* q, const void* k, const void* v, const void* out,
+                                                 const void* dout, const float* lse, const int32_t* doc_ids,
+                                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                                 int64_t D, int64_t seq_start, int64_t kv_start, int64_t kv_len,
+                                                 float scale, int32_t enable_gqa, void* dq, void* dk, void* dv,
+                                                 void* workspace, size_t workspace_bytes, int32_t* status_word,
+                                                 void* stream);
+
+/*
+ * Start of the key window a query shard needs, per row (blockdiag_cp page, package
+ * overview: needed-only key delivery through a left halo).  kv_start_out[b] =
+ * min(seq_start, first position of the document of the shard's first non-padding row);
+ * seq_start when the shard has no such row.  The halo a rank receives from earlier
+ * ranks is [kv_start_out[b], seq_start).
+ *
+ *   doc_ids       device int32 [B, S], contiguous; each non-padding id one run per row.
+ *   kv_start_out  device int32 [B] (written).
+ * 0 <= seq_start, seq_start + L <= S (else PSB_ERR_SHAPE).  B == 0 enqueues nothing.
+ */
+psb_status psb_shard_kv_window_start(const int32_t* doc_ids, int64_t B, int64_t S, int64_t seq_start, int64_t L,
+                                     int32_t* kv_start_out, void* stream);
 
 #ifdef __cplusplus
 }

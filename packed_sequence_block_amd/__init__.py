@@ -10,10 +10,16 @@ Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
 * :func:`blockdiag_attn_fwd_lse` / :func:`blockdiag_attn_bwd` — the training
   path (forward with per-row log-sum-exp, then dq, dk, dv);
   :func:`blockdiag_attention` wraps both as a torch autograd function.
+* :func:`shard_kv_window_start`, :func:`blockdiag_attn_fwd_window` /
+  :func:`blockdiag_attn_bwd_window` — a query shard run against a delivered key
+  window (its own keys plus a left halo) instead of the whole row.
+* :func:`doc_ids_from_seq_lens`, :func:`unpack_row_layout`,
+  :func:`validate_document_positions` — layouts from packed length tables.
 """
 
 from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd, blockdiag_attn_fwd_lse,
                    bwd_workspace_size, doc_ids_from_cu_seqlens, doc_ids_from_seq_lens, load,
+                   blockdiag_attn_bwd_window, blockdiag_attn_fwd_window, shard_kv_window_start,
                    segment_cu_seqlens, status_string, unpack_row_layout, unpack_row_layout_batch, validate_doc_ids,
                    validate_document_positions,
                    workspace_size)
@@ -22,6 +28,7 @@ from .autograd import blockdiag_attention
 
 __all__ = ["blockdiag_attention", "PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
            "bwd_workspace_size", "doc_ids_from_cu_seqlens", "doc_ids_from_seq_lens", "load",
+           "blockdiag_attn_bwd_window", "blockdiag_attn_fwd_window", "shard_kv_window_start",
            "segment_cu_seqlens", "status_string", "unpack_row_layout", "unpack_row_layout_batch", "validate_doc_ids",
            "validate_document_positions",
            "workspace_size"]

@@ -28,6 +28,7 @@ DATA_DOC_NOT_CONTIGUOUS = 4
 DATA_LENS_EXCEED_SEQ = 8
 DATA_BAD_POSITIONS = 16
 DATA_BAD_LENGTHS = 32
+DATA_KV_WINDOW = 64
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -43,6 +44,14 @@ SIGNATURES = {
     "psb_doc_ids_from_seq_lens": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _vp, _vp]),
     "psb_validate_document_positions": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
     "psb_unpack_row_layout": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "psb_shard_kv_window_start": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "psb_blockdiag_attn_fwd_window_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                       _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, ctypes.c_float,
+                                                       _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]),
+    "psb_blockdiag_attn_bwd_window_planned": (_c_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                                       _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                       ctypes.c_float, _c_i32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                                       _vp, _vp]),
     "psb_blockdiag_attn_fwd_workspace_size": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
     "psb_blockdiag_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, ctypes.c_size_t,
@@ -367,3 +376,88 @@ def validate_document_positions(keep: torch.Tensor, positions: torch.Tensor) -> 
                                                   _vp(_stream(k))), "validate_document_positions")
     if int(status.item()) != 0:
         raise ValueError("positions break the document rule")
+
+
+# ---- query shard against a delivered key window (left-halo delivery) -------------------
+
+def shard_kv_window_start(doc_ids: torch.Tensor, seq_start: int, L: int) -> torch.Tensor:
+    """Per row, the first key position the query shard ``[seq_start, seq_start + L)``
+    needs (``[B]`` int32, on the device): ``min(seq_start, start of the document of the
+    shard's first non-padding row)``."""
+    _need_gpu(doc_ids)
+    ids = doc_ids.reshape(doc_ids.shape[0] if doc_ids.dim() > 1 else 1, -1)
+    ids = (ids if ids.dtype == torch.int32 else ids.to(torch.int32)).contiguous()
+    B, S = ids.shape
+    out = torch.empty(B, dtype=torch.int32, device=ids.device)
+    _check(load().psb_shard_kv_window_start(_ptr(ids), B, S, int(seq_start), int(L), _ptr(out), _vp(_stream(ids))),
+           "shard_kv_window_start")
+    return out
+
+
+def _window_status(status, where):
+    if status is not None and int(status.item()) & DATA_KV_WINDOW:
+        raise ValueError(f"{where}: a query row needs a key before the delivered window")
+
+
+def blockdiag_attn_fwd_window(q, k, v, doc_ids, seq_start: int, kv_start: int, scale: float | None = None,
+                              enable_gqa: bool = False, with_lse: bool = False,
+                              workspace: torch.Tensor | None = None, validate: bool = False):
+    """Forward of a query shard against the keys ``[kv_start, kv_start + kv_len)``.
+
+    ``k, v [B, Hkv, kv_len, D]`` (contiguous) hold just that window; ``doc_ids [B, S]``
+    covers the whole rows.  Returns ``out``, or ``(out, lse, workspace)`` with
+    ``with_lse=True`` (the workspace then serves :func:`blockdiag_attn_bwd_window`).
+    ``validate=True`` synchronizes and raises ``ValueError`` when some row needs a key
+    before ``kv_start``.
+    """
+    _need_gpu(q, k, v, doc_ids)
+    _check_qkv(q, k, v, contiguous=True)
+    B, Hq, L, D = q.shape
+    Hkv, kv_len = k.shape[1], k.shape[2]
+    S = doc_ids.shape[-1]
+    ids = _ids(doc_ids, B, S)
+    need = bwd_workspace_size(B, Hq, Hkv, L, S, D) if with_lse else workspace_size(B, Hq, Hkv, L, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if with_lse else None
+    status = torch.zeros(1, dtype=torch.int32, device=q.device) if validate else None
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    gqa = 1 if enable_gqa else 0
+    st = _vp(_stream(q))
+    lib = load()
+    _check(lib.psb_blockdiag_attn_plan(_ptr(ids), B, Hq, Hkv, L, S, D, int(seq_start), gqa, _ptr(workspace),
+                                       need, st), "blockdiag_attn_plan")
+    _check(lib.psb_blockdiag_attn_fwd_window_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(ids), B, Hq, Hkv, L, S, D, None, None, int(seq_start), int(kv_start),
+        kv_len, sc, gqa, _ptr(out), _ptr(lse), _ptr(workspace), need, _ptr(status), st),
+        "blockdiag_attn_fwd_window_planned")
+    _window_status(status, "blockdiag_attn_fwd_window")
+    return (out, lse, workspace) if with_lse else out
+
+
+def blockdiag_attn_bwd_window(q, k, v, out, dout, lse, doc_ids, workspace, seq_start: int, kv_start: int,
+                              scale: float | None = None, enable_gqa: bool = False, validate: bool = False):
+    """Gradients ``(dq, dk, dv)`` of the windowed forward; ``dk, dv [B, Hkv, kv_len, D]``
+    are the gradients of the window's keys (this shard's rows only)."""
+    _need_gpu(q, k, v, out, dout, lse, doc_ids, workspace)
+    _check_qkv(q, k, v, contiguous=True)
+    B, Hq, L, D = q.shape
+    Hkv, kv_len = k.shape[1], k.shape[2]
+    S = doc_ids.shape[-1]
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like q")
+    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, L] tensor")
+    ids = _ids(doc_ids, B, S)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    status = torch.zeros(1, dtype=torch.int32, device=q.device) if validate else None
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().psb_blockdiag_attn_bwd_window_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(ids), B, Hq, Hkv, L, S, D,
+        int(seq_start), int(kv_start), kv_len, sc, 1 if enable_gqa else 0, _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), nbytes, _ptr(status), _vp(_stream(q))), "blockdiag_attn_bwd_window_planned")
+    _window_status(status, "blockdiag_attn_bwd_window")
+    return dq, dk, dv

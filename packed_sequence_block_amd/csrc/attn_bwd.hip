@@ -46,14 +46,14 @@ constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgro
 
 struct BwdParams {
   const __bf16* q;     // [B, Hq, L, D]
-  const __bf16* k;     // [B, Hkv, S, D]
+  const __bf16* k;     // [B, Hkv, kv_len, D]: keys at global positions [kv_start, kv_start + kv_len)
   const __bf16* v;
   const __bf16* dout;  // [B, Hq, L, D]
   const float* lse;    // [B, Hq, L] natural log
   const float* delta;  // [B, Hq, L]
   const int32_t* doc;  // [B, S]
   __bf16* dq;          // [B, Hq, L, D]
-  __bf16* dk;          // [B, Hkv, S, D]
+  __bf16* dk;          // [B, Hkv, kv_len, D]
   __bf16* dv;
   int32_t B, Hq, Hkv, L, S, seq_start, group;
   int32_t nblk, ntile_row, units;
@@ -63,6 +63,8 @@ struct BwdParams {
   const TileRecord* work;
   const TileRecord* kwork;  // key tiles, longest row range first
   int32_t nkt;              // key tiles per batch row
+  int32_t kv_start, kv_len;
+  int32_t* status;          // PSB_DATA_KV_WINDOW when a row needs a key before kv_start, or null
 };
 
 // ---- delta = rowsum(dO * O) --------------------------------------------------------
@@ -133,7 +135,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     const int32_t row_local = blk * kRowsPerBlock + lr;
     const bool row_in = blk < p.nblk && row_local < p.L;
     const int32_t qpos = p.seq_start + row_local;
-    const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
+    const int32_t tlo = max(rec.lo, p.kv_start), thi = min(rec.hi, p.kv_start + p.kv_len);
+    if (p.status != nullptr && tid == 0 && rec.hi > rec.lo && rec.lo < p.kv_start)
+      atomicOr(p.status, PSB_DATA_KV_WINDOW);
     const int64_t qrow = ((int64_t)b * p.Hq + hq) * p.L + row_local;
     __bf16* dq_row = p.dq + qrow * D;
     if (thi <= tlo) {
@@ -147,11 +151,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       continue;
     }
     const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
-    const __bf16* kbase = p.k + ((int64_t)b * p.Hkv + g) * p.S * D;
-    const __bf16* vbase = p.v + ((int64_t)b * p.Hkv + g) * p.S * D;
+    const __bf16* kbase = p.k + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
+    const __bf16* vbase = p.v + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
     auto issue = [&](const __bf16* base, __bf16* buf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(base + (int64_t)kt * D), (short)0, min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+          (void*)(base + (int64_t)(kt - p.kv_start) * D), (short)0, min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
       for (int j = 0; j < KSEG_ITERS; ++j) {
         const int seg = j * kBwdWaves + wv;
@@ -341,8 +345,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     const int32_t g = (int32_t)(item % p.Hkv);
     const int32_t b = rec.b, kt_i = rec.rt;
     if (b < 0 || b >= p.B || kt_i < 0 || kt_i >= nkt) continue;  // workspace from another plan
-    const int32_t key = kt_i * kKeysPerItem + kKeysPerWave * wv + lr;
-    const bool key_in = key < p.S;
+    const int32_t key = p.kv_start + kt_i * kKeysPerItem + kKeysPerWave * wv + lr;  // global position
+    const bool key_in = key < p.kv_start + p.kv_len;
     const int32_t* docrow = p.doc + (int64_t)b * p.S;
 
     // ---- this lane's key: the rows that see it -------------------------------------------
@@ -356,7 +360,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     {
       const uint64_t from = lm & ~((1ull << lr) - 1ull);       // run ends at or after this key
       const int e = __ffsll((unsigned long long)from) - 1;      // lane of this run's last key
-      const int32_t wkey0 = __builtin_amdgcn_readfirstlane(kt_i * kKeysPerItem + kKeysPerWave * wv);
+      const int32_t wkey0 =
+          __builtin_amdgcn_readfirstlane(p.kv_start + kt_i * kKeysPerItem + kKeysPerWave * wv);
       int32_t tail_end = 0;
       {
         // run end after the wave's last key (lane 31); the search is wave-uniform
@@ -408,7 +413,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     // ---- stationary K^T and V^T operands (B operands: lane = key) --------------------------
     bf16x8 kreg[KS], vreg[KS];
     {
-      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.S + key;
+      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (key_in) {
@@ -542,7 +547,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
 
     // ---- epilogue: C[d][key] -> dk, dv rows (lane = key, 4 consecutive d per store) -------
     if (key_in) {
-      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.S + key;
+      const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
       __bf16* dkr = p.dk + kvrow * D;
       __bf16* dvr = p.dv + kvrow * D;
 #pragma unroll
@@ -591,7 +596,8 @@ hipError_t launch_bwd(int nh, const BwdParams& prm, const __bf16* out, float* de
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t kgrid = (int64_t)prm.B * prm.Hkv * ((prm.S + kKeysPerItem - 1) / kKeysPerItem);
+  const int64_t kgrid = (int64_t)prm.B * prm.Hkv * ((prm.kv_len + kKeysPerItem - 1) / kKeysPerItem);
+  if (kgrid == 0) return hipSuccess;
   dkdv_kernel<D><<<dim3((unsigned)kgrid), dim3(kBwdThreads), 0, s>>>(prm);
   return hipGetLastError();
 }
@@ -608,20 +614,24 @@ PSB_API size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int6
   return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L) + key_schedule_bytes(B, S));
 }
 
-PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
-                                                  const void* dout, const float* lse, const int32_t* doc_ids,
-                                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
-                                                  int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
-                                                  void* dq, void* dk, void* dv, void* workspace,
-                                                  size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;
+namespace {
+
+// The backward with k, v, dk, dv holding the keys [kv_start, kv_start + kv_len) of each row.
+psb_status bwd_run(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                   const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S, int64_t D,
+                   int64_t seq_start, int64_t kv_start, int64_t kv_len, float scale, int32_t enable_gqa, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 0 || L < 0 || S < 0 || D < 0 || seq_start < 0) return PSB_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PSB_ERR_UNSUPPORTED;
   if (Hq > 0 && Hkv == 0) return PSB_ERR_SHAPE;
   if (enable_gqa ? (Hkv > 0 && Hq % Hkv != 0) : (Hq != Hkv)) return PSB_ERR_SHAPE;
   if (seq_start + L > S) return PSB_ERR_SHAPE;
   if (L >= INT32_MAX || S >= INT32_MAX || Hq >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
-  if (B == 0 || Hq == 0 || S == 0) return PSB_OK;
+  // the window holds the shard's own keys and lies inside the row
+  if (kv_start < 0 || kv_len < 0 || kv_start > seq_start || kv_start + kv_len < seq_start + L ||
+      kv_start + kv_len > S)
+    return PSB_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || kv_len == 0) return PSB_OK;
   if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
   const void* kv_side[] = {k, v, dk, dv, workspace};
   for (const void* ptr : kv_side)
@@ -639,7 +649,7 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
   const int64_t nr = kBwdWaves / nh;
   const int64_t ntiles = (L > 0) ? schedule_ntiles(B, L, nr) : 0;
   const int64_t units = Hq / nh;
-  if (ntiles * units >= INT32_MAX || B * Hkv * ((S + kKeysPerItem - 1) / kKeysPerItem) >= INT32_MAX)
+  if (ntiles * units >= INT32_MAX || B * Hkv * ((kv_len + kKeysPerItem - 1) / kKeysPerItem) >= INT32_MAX)
     return PSB_ERR_SHAPE;
   const ScheduleBuffers buf = schedule_carve(workspace, B, L, nr);
   char* wsb = static_cast<char*>(workspace);
@@ -669,13 +679,41 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
   prm.items = ntiles * units;
   prm.work = buf.work;
   prm.kwork = kwork;
-  prm.nkt = (int32_t)((S + kKeyTile - 1) / kKeyTile);
+  prm.nkt = (int32_t)((kv_len + kKeyTile - 1) / kKeyTile);
+  prm.kv_start = (int32_t)kv_start;
+  prm.kv_len = (int32_t)kv_len;
+  prm.status = status;
   const int64_t rows = B * Hq * L;
-  if (launch_key_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, klo, khi, kwork,
-                          as_stream(stream)) != hipSuccess)
+  if (launch_key_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, (int32_t)kv_start,
+                          (int32_t)kv_len, klo, khi, kwork, as_stream(stream)) != hipSuccess)
     return PSB_ERR_HIP;
   const hipError_t e = (D == 128)
       ? launch_bwd<128>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream))
       : launch_bwd<64>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream));
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
+}
+
+}  // namespace
+
+PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
+                                                  const void* dout, const float* lse, const int32_t* doc_ids,
+                                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
+                                                  int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
+                                                  void* dq, void* dk, void* dv, void* workspace,
+                                                  size_t workspace_bytes, int32_t* status_word, void* stream) {
+  (void)status_word;  // no data check in this call
+  return bwd_run(q, k, v, out, dout, lse, doc_ids, B, Hq, Hkv, L, S, D, seq_start, 0, S, scale, enable_gqa, dq, dk,
+                 dv, workspace, workspace_bytes, nullptr, stream);
+}
+
+PSB_API psb_status psb_blockdiag_attn_bwd_window_planned(const void* q, const void* k, const void* v,
+                                                         const void* out, const void* dout, const float* lse,
+                                                         const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                                         int64_t L, int64_t S, int64_t D, int64_t seq_start,
+                                                         int64_t kv_start, int64_t kv_len, float scale,
+                                                         int32_t enable_gqa, void* dq, void* dk, void* dv,
+                                                         void* workspace, size_t workspace_bytes,
+                                                         int32_t* status_word, void* stream) {
+  return bwd_run(q, k, v, out, dout, lse, doc_ids, B, Hq, Hkv, L, S, D, seq_start, kv_start, kv_len, scale,
+                 enable_gqa, dq, dk, dv, workspace, workspace_bytes, status_word, stream);
 }

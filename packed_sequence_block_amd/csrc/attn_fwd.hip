@@ -51,12 +51,14 @@ struct AttnParams {
   __bf16* out;
   int64_t q_sb, q_sh, q_ss;
   int64_t kv_sb, kv_sh, kv_ss;
+  int32_t kv_start, kv_end;  // k / v hold the keys at global positions [kv_start, kv_end)
   int32_t B, Hq, Hkv, L, S, seq_start, group;
   int32_t nblk, ntile_row, units;
   float sc;  // softmax scale * log2(e)
   int64_t items;  // row tiles x head units
   const TileRecord* work;
   float* lse;     // [B, Hq, L] natural-log sum of exp(scale * q.k) per row, or null
+  int32_t* status;  // PSB_DATA_KV_WINDOW when a row needs a key before kv_start, or null
 };
 
 // the running row max is only moved (and O, l rescaled) when a tile's max exceeds
@@ -147,7 +149,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const int32_t row_local = blk * kRowsPerBlock + lr;
     const bool row_in = blk < p.nblk && row_local < p.L;
     const int32_t qpos = p.seq_start + row_local;
-    const int32_t tlo = max(rec.lo, 0), thi = min(rec.hi, p.S);
+    // keys outside the delivered window are never loaded; a row that needs one (the
+    // window does not reach back to its document start) is reported
+    const int32_t tlo = max(rec.lo, p.kv_start), thi = min(rec.hi, p.kv_end);
+    if (p.status != nullptr && tid == 0 && rec.hi > rec.lo && rec.lo < p.kv_start)
+      atomicOr(p.status, PSB_DATA_KV_WINDOW);
     __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
 
     if (thi <= tlo) {  // no valid query row in the whole tile: outputs are 0, lse -inf
@@ -168,7 +174,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
     auto issue_k = [&](__bf16* kbuf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + (int64_t)kt * p.kv_ss), (short)0,
+          (void*)(kbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
           min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
       for (int j = 0; j < KSEG_ITERS; ++j) {
@@ -178,7 +184,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     };
     auto issue_v = [&](__bf16* vbuf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + (int64_t)kt * p.kv_ss), (short)0,
+          (void*)(vbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
           min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
 #pragma unroll
       for (int j = 0; j < VSEG_ITERS; ++j) {
@@ -461,13 +467,14 @@ psb_status plan_impl(const int32_t* doc_ids, int64_t B, int64_t L, int64_t S, in
 
 psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids, int64_t B, int64_t Hq,
                     int64_t Hkv, int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
-                    const int64_t* kv_strides, int64_t seq_start, float scale, const AttnGeometry& geo, void* out,
-                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t s) {
+                    const int64_t* kv_strides, int64_t seq_start, int64_t kv_start, int64_t kv_len, float scale,
+                    const AttnGeometry& geo, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    int32_t* status, hipStream_t s) {
   if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
   if (q == nullptr || k == nullptr || v == nullptr || doc_ids == nullptr || out == nullptr || workspace == nullptr)
     return PSB_ERR_INVALID_ARG;
   const int64_t qs_def[3] = {Hq * L * D, L * D, D};
-  const int64_t kvs_def[3] = {Hkv * S * D, S * D, D};
+  const int64_t kvs_def[3] = {Hkv * kv_len * D, kv_len * D, D};
   const int64_t* qs = q_strides ? q_strides : qs_def;
   const int64_t* kvs = kv_strides ? kv_strides : kvs_def;
   for (int i = 0; i < 3; ++i) {
@@ -477,6 +484,7 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
     return PSB_ERR_INVALID_ARG;
+  (void)S;
   if (workspace_bytes < (size_t)schedule_bytes(B, L, geo.nr)) return PSB_ERR_CAPACITY;
   const ScheduleBuffers buf = schedule_carve(workspace, B, L, geo.nr);
   AttnParams prm;
@@ -487,6 +495,7 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   prm.out = static_cast<__bf16*>(out);
   prm.q_sb = qs[0]; prm.q_sh = qs[1]; prm.q_ss = qs[2];
   prm.kv_sb = kvs[0]; prm.kv_sh = kvs[1]; prm.kv_ss = kvs[2];
+  prm.kv_start = (int32_t)kv_start; prm.kv_end = (int32_t)(kv_start + kv_len);
   prm.B = (int32_t)B; prm.Hq = (int32_t)Hq; prm.Hkv = (int32_t)Hkv; prm.L = (int32_t)L; prm.S = (int32_t)S;
   prm.seq_start = (int32_t)seq_start; prm.group = (int32_t)geo.group;
   prm.nblk = (int32_t)schedule_nblk(L);
@@ -496,6 +505,7 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   prm.items = geo.grid;
   prm.work = buf.work;
   prm.lse = lse;
+  prm.status = status;
   // one workgroup per item: the dispatcher starts a new one whenever a slot frees,
   // which balances the longest-first order better than a fixed persistent split
   const int64_t grid = geo.grid;
@@ -533,13 +543,13 @@ PSB_API psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, 
                                                   const int64_t* kv_strides, int64_t seq_start, float scale,
                                                   int32_t enable_gqa, void* out, const void* workspace,
                                                   size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;
+  (void)status_word;  // no data check in this call
   AttnGeometry geo;
   const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
-                  nullptr, const_cast<void*>(workspace), workspace_bytes, as_stream(stream));
+  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                  nullptr, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, const void* v,
@@ -549,14 +559,14 @@ PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void*
                                                       int32_t enable_gqa, void* out, float* lse,
                                                       const void* workspace, size_t workspace_bytes,
                                                       int32_t* status_word, void* stream) {
-  (void)status_word;
+  (void)status_word;  // no data check in this call
   AttnGeometry geo;
   const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
-                  lse, const_cast<void*>(workspace), workspace_bytes, as_stream(stream));
+  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                  lse, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
@@ -564,7 +574,7 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
                                           const int64_t* q_strides, const int64_t* kv_strides, int64_t seq_start,
                                           float scale, int32_t enable_gqa, void* out, void* workspace,
                                           size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;
+  (void)status_word;  // no data check in this call
   AttnGeometry geo;
   psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
@@ -585,6 +595,27 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
   hipStream_t s = as_stream(stream);
   st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
   if (st != PSB_OK) return st;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, geo, out,
-                  nullptr, workspace, workspace_bytes, s);
+  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                  nullptr, workspace, workspace_bytes, nullptr, s);
+}
+
+PSB_API psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const void* k, const void* v,
+                                                         const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                                         int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                                         const int64_t* kv_strides, int64_t seq_start,
+                                                         int64_t kv_start, int64_t kv_len, float scale,
+                                                         int32_t enable_gqa, void* out, float* lse,
+                                                         const void* workspace, size_t workspace_bytes,
+                                                         int32_t* status_word, void* stream) {
+  AttnGeometry geo;
+  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  if (st != PSB_OK) return st;
+  // the window holds the shard's own keys and reaches back no further than position 0
+  if (kv_start < 0 || kv_len < 0 || kv_start > seq_start || kv_start + kv_len < seq_start + L ||
+      kv_start + kv_len > S)
+    return PSB_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
+  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, kv_start, kv_len, scale,
+                  geo, out, lse, const_cast<void*>(workspace), workspace_bytes, status_word, as_stream(stream));
 }

@@ -50,8 +50,9 @@ inline ScheduleBuffers schedule_carve(void* ws, int64_t B, int64_t L, int64_t nr
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
                            int32_t nr, const ScheduleBuffers& buf, hipStream_t stream);
 
-// Backward key side: tiles of kKeyTile keys, each with the local query rows that see
-// its keys, ordered by row-range length (longest first).
+// Backward key side: tiles of kKeyTile keys of the window [kv_start, kv_start + kv_len),
+// each with the local query rows that see its keys, ordered by row-range length
+// (longest first).  The tables are sized for the whole row (kv_len <= S).
 //   klo/khi [B * nkt], work [B * nkt] (records with b = batch row, rt = key tile)
 constexpr int kKeyTile = 128;
 inline int64_t key_ntiles(int64_t B, int64_t S) { return B * ((S + kKeyTile - 1) / kKeyTile); }
@@ -59,6 +60,7 @@ inline int64_t key_schedule_bytes(int64_t B, int64_t S) {
   return 2 * pad256(4 * key_ntiles(B, S)) + pad256(64 * key_ntiles(B, S));
 }
 hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
-                               int32_t* klo, int32_t* khi, TileRecord* work, hipStream_t stream);
+                               int32_t kv_start, int32_t kv_len, int32_t* klo, int32_t* khi, TileRecord* work,
+                               hipStream_t stream);
 
 }  // namespace psb

@@ -135,23 +135,25 @@ __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t*
 }
 
 // ---- key side (backward dK / dV) -----------------------------------------------------
-// One wave per tile of kKeyTile keys: the local query rows that see any of its keys,
+// One wave per tile of kKeyTile keys of the window [kv_start, kv_end) (tile t starts at
+// kv_start + t * kKeyTile): the local query rows that see any of its keys,
 // [max(first valid key, seq_start), min(end of the last valid key's document,
 // seq_start + L)) - seq_start (key k is seen by the rows of its document at or after
 // k; the run end is found by a 64-way search).  Empty tiles get (0, 0).
 __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restrict__ doc_ids, int32_t S, int32_t L,
-                                                        int32_t seq_start, int32_t nkt, int32_t total,
-                                                        int32_t* __restrict__ klo, int32_t* __restrict__ khi) {
+                                                        int32_t seq_start, int32_t kv_start, int32_t kv_end,
+                                                        int32_t nkt, int32_t total, int32_t* __restrict__ klo,
+                                                        int32_t* __restrict__ khi) {
   const int32_t wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (wid >= total) return;
   const int32_t b = wid / nkt, kt = wid % nkt;
   const int32_t* row = doc_ids + (int64_t)b * S;
-  const int32_t k0 = kt * kKeyTile;
+  const int32_t k0 = kv_start + kt * kKeyTile;
   static_assert(kKeyTile == 2 * kWave, "two keys per lane");
   const int32_t ka = k0 + lane, kb = k0 + kWave + lane;
-  const bool va = ka < S && row[ka] != PSB_PAD_DOC_ID;
-  const bool vb = kb < S && row[kb] != PSB_PAD_DOC_ID;
+  const bool va = ka < kv_end && row[ka] != PSB_PAD_DOC_ID;
+  const bool vb = kb < kv_end && row[kb] != PSB_PAD_DOC_ID;
   const uint64_t ma = __ballot(va), mb = __ballot(vb);
   if ((ma | mb) == 0) {
     if (lane == 0) { klo[wid] = 0; khi[wid] = 0; }
@@ -183,6 +185,49 @@ __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restric
   }
 }
 
+// ---- key window of a query shard ----------------------------------------------------
+// One wave per batch row: the first non-padding row of the shard (64 rows per ballot),
+// then the start of its document by the same 64-way search as block_range_kernel.
+__global__ void __launch_bounds__(256) shard_window_kernel(const int32_t* __restrict__ doc_ids, int32_t B, int32_t S,
+                                                           int32_t seq_start, int32_t L,
+                                                           int32_t* __restrict__ kv_start_out) {
+  const int32_t b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (b >= B) return;
+  const int32_t* row = doc_ids + (int64_t)b * S;
+  int32_t qf = -1;
+  for (int32_t r0 = 0; r0 < L; r0 += kWave) {
+    const int32_t r = r0 + lane;
+    const uint64_t m = __ballot(r < L && row[seq_start + r] != PSB_PAD_DOC_ID);
+    if (m != 0) {
+      qf = seq_start + r0 + __ffsll((unsigned long long)m) - 1;
+      break;
+    }
+  }
+  int32_t lo = seq_start;
+  if (qf >= 0) {
+    const int32_t x = row[qf];
+    int32_t hi = qf;  // the document start lies in [lo, hi]; doc[hi] == x
+    lo = 0;
+    while (lo < hi) {
+      const int32_t step = (hi - lo + kWave - 1) / kWave;
+      int32_t p = lo + lane * step;
+      if (p > hi) p = hi;
+      const uint64_t t = __ballot(row[p] == x);
+      if (t == 0) {
+        lo = lo + (kWave - 1) * step + 1;
+      } else {
+        const int32_t i = __ffsll((unsigned long long)t) - 1;
+        const int32_t pi = min(hi, lo + i * step);
+        lo = (i == 0) ? lo : lo + (i - 1) * step + 1;
+        hi = pi;
+      }
+    }
+    lo = min(lo, seq_start);
+  }
+  if (lane == 0) kv_start_out[b] = lo;
+}
+
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
@@ -206,12 +251,15 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
 namespace psb {
 
 hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
-                               int32_t* klo, int32_t* khi, TileRecord* work, hipStream_t stream) {
-  const int32_t nkt = (S + kKeyTile - 1) / kKeyTile;
+                               int32_t kv_start, int32_t kv_len, int32_t* klo, int32_t* khi, TileRecord* work,
+                               hipStream_t stream) {
+  const int32_t nkt = (kv_len + kKeyTile - 1) / kKeyTile;
   const int32_t total = B * nkt;
+  if (total == 0) return hipSuccess;
   const int waves_per_wg = 256 / kWave;
   const int32_t grid = (total + waves_per_wg - 1) / waves_per_wg;
-  key_range_kernel<<<dim3(grid), dim3(256), 0, stream>>>(doc_ids, S, L, seq_start, nkt, total, klo, khi);
+  key_range_kernel<<<dim3(grid), dim3(256), 0, stream>>>(doc_ids, S, L, seq_start, kv_start, kv_start + kv_len, nkt,
+                                                         total, klo, khi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // longest row range first, as for the query side (records with nr = 1: one key tile each)
@@ -220,3 +268,18 @@ hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int
 }
 
 }  // namespace psb
+
+using namespace psb;
+
+PSB_API psb_status psb_shard_kv_window_start(const int32_t* doc_ids, int64_t B, int64_t S, int64_t seq_start,
+                                             int64_t L, int32_t* kv_start_out, void* stream) {
+  if (B < 0 || S < 0 || L < 0 || seq_start < 0) return PSB_ERR_INVALID_ARG;
+  if (seq_start + L > S || S >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (B == 0) return PSB_OK;
+  if (kv_start_out == nullptr || (L > 0 && doc_ids == nullptr)) return PSB_ERR_INVALID_ARG;
+  const int64_t grid = (B + 3) / 4;
+  shard_window_kernel<<<dim3((unsigned)grid), dim3(256), 0, as_stream(stream)>>>(
+      doc_ids, (int32_t)B, (int32_t)S, (int32_t)seq_start, (int32_t)L, kv_start_out);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
