@@ -43,12 +43,12 @@ worked examples under ``tests/golden``).
 from .boundary import (PAD_DOC_ID, doc_ids_from_cu_seqlens, doc_ids_from_seq_lens, document_positions_valid,
                        segment_cu_seqlens, unpack_row_layout)
 from .attention import (allowed_mask, blockdiag_attn, blockdiag_attn_loop, blockdiag_attn_rows,
-                        kv_head_of, kv_window_start)
+                        dense_mask, kv_head_of, kv_window_start, masked_attn)
 
 __all__ = [
     "PAD_DOC_ID", "doc_ids_from_cu_seqlens", "segment_cu_seqlens", "doc_ids_from_seq_lens",
     "document_positions_valid", "unpack_row_layout",
     "allowed_mask", "blockdiag_attn", "blockdiag_attn_loop", "blockdiag_attn_rows", "kv_head_of",
-    "kv_window_start",
+    "kv_window_start", "dense_mask", "masked_attn",
 ]
 from .attention_bwd import blockdiag_attn_bwd, blockdiag_attn_lse

@@ -195,3 +195,46 @@ def kv_window_start(doc_ids, seq_start: int, L: int) -> np.ndarray:
         if cols.numel() > 0:
             out[b] = min(seq_start, int(cols[0]))
     return out
+
+
+def dense_mask(doc_ids, seq_start: int, L: int) -> torch.Tensor:
+    """The per-document causal mask materialised, bool ``[B, L, S]`` (True = may attend).
+
+    blockdiag_cp page, package overview: the ``.kernels`` layer has a dense-mask path
+    next to the varlen kernels; this is the mask such a path consumes, row i of the
+    shard being global position ``seq_start + i``.
+    """
+    doc_ids = torch.as_tensor(np.asarray(doc_ids)).to(torch.int64)
+    doc_ids = doc_ids.reshape(doc_ids.shape[0], -1)
+    qpos = torch.arange(seq_start, seq_start + L, dtype=torch.int64)
+    return torch.stack([allowed_mask(doc_ids[b], qpos) for b in range(doc_ids.shape[0])])
+
+
+def masked_attn(q, k, v, mask, scale: float | None = None, enable_gqa: bool = False) -> torch.Tensor:
+    """Attention under an explicit boolean mask, fp64 ``[B, Hq, L, D]``.
+
+    ``mask`` is ``[B, L, S]`` (or ``[1, L, S]``, shared by the batch), True where
+    query row i may attend to key j, the same for every head; a row with no allowed
+    key outputs 0.  Scale and GQA as in ``blockdiag_attn``.
+    """
+    mask = torch.as_tensor(np.asarray(mask)).to(torch.bool)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k / v shape does not match q")
+    if enable_gqa:
+        if Hq % Hkv != 0:
+            raise ValueError("Hq must be a multiple of Hkv")
+    elif Hq != Hkv:
+        raise ValueError("Hq != Hkv needs enable_gqa")
+    if mask.dim() != 3 or mask.shape[1:] != (L, S) or mask.shape[0] not in (1, B):
+        raise ValueError("mask must be [B or 1, L, S]")
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
+    out = torch.zeros((B, Hq, L, D), dtype=torch.float64)
+    for b in range(B):
+        mb = mask[b if mask.shape[0] == B else 0]
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            out[b, h] = _softmax_weighted_mean((qf[b, h] @ kf[b, g].T) * sc, mb, vf[b, g])
+    return out
