@@ -142,6 +142,37 @@ def window_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
             "ms": round(ms, 5), "useful_tflops": round(lay.useful_flops() / (ms * 1e-3) / 1e12, 3)}
 
 
+def dense_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
+    """The dense-mask path on the same workload: the per-document mask materialised,
+    then attention under that explicit mask (every key tile of every row visited)."""
+    import torch
+    B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
+    stride = (S + 15) // 16 * 16
+    mask = torch.empty((B, L, stride), dtype=torch.bool, device=q.device)
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def build():
+        assert lib.psb_blockdiag_dense_mask(P(doc_ids), B, S, lay.seq_start, L, P(mask), stride, sptr) == 0
+
+    def attn():
+        st = lib.psb_masked_attn_fwd(P(q), P(k), P(v), P(mask), L * stride, stride, B, Hq, Hkv, L, S, D, None, None,
+                                     float(D) ** -0.5, 1 if lay.enable_gqa else 0, P(out), None, sptr)
+        assert st == 0, st
+
+    build()
+    attn()
+    torch.cuda.synchronize()
+    n = max(3, steps // 5)
+    mask_ms, attn_ms = timed(build, n), timed(attn, n)
+    visited = 4.0 * D * Hq * B * L * S
+    return {"what": "materialised per-document mask + attention under it", "mask_ms": round(mask_ms, 5),
+            "attention_ms": round(attn_ms, 5), "mask_bytes": B * L * stride,
+            "useful_tflops": round(lay.useful_flops() / ((mask_ms + attn_ms) * 1e-3) / 1e12, 3),
+            "visited_tflops": round(visited / (attn_ms * 1e-3) / 1e12, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +181,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-path (backward) timing")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-mask path timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -256,6 +288,8 @@ def main():
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
         "phase_ms": phase_ms,
     }
+    if not args.no_dense:
+        rec["dense_mask"] = dense_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     rec["kv_window"] = window_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     if not args.no_backward:
         rec["backward"] = backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)

@@ -349,6 +349,39 @@ psb_status psb_blockdiag_attn_bwd_window_planned(const void* q, const void* k, c
 psb_status psb_shard_kv_window_start(const int32_t* doc_ids, int64_t B, int64_t S, int64_t seq_start, int64_t L,
                                      int32_t* kv_start_out, void* stream);
 
+/*
+ * The dense-mask path (blockdiag_cp page, package overview: the kernels layer has a
+ * dense-mask kernel next to the varlen ones).
+ *
+ * psb_blockdiag_dense_mask materialises the per-document causal mask of a query shard:
+ *   mask_out[b][i][k] = 1 iff doc_ids[b,k] == doc_ids[b,q], doc_ids[b,q] != -1000 and
+ *   k <= q, for q = seq_start + i; else 0 (also for the padding bytes S..row_stride-1).
+ *   doc_ids     device int32 [B, S], contiguous.
+ *   mask_out    device uint8 [B, L, row_stride], contiguous, 4-byte aligned;
+ *               row_stride >= S and a multiple of 4 (else PSB_ERR_SHAPE).
+ *
+ * psb_masked_attn_fwd is attention under an explicit mask, the same for all heads:
+ *   out[b,h,i] = softmax over the keys k with mask[b][i][k] != 0 of scale * q.k, times v;
+ *   a row without such a key outputs 0 (and lse -inf).
+ *   q            device bf16 [B, Hq, L, D] (q_strides, elements, or NULL = contiguous).
+ *   k, v         device bf16 [B, Hkv, S, D] (kv_strides likewise).  L and S independent.
+ *   mask         device uint8, row i of batch b at mask + b * mask_batch_stride +
+ *                i * mask_row_stride (bytes; batch stride 0 shares one mask); 4-byte
+ *                aligned, both strides multiples of 4, and every row readable up to S
+ *                rounded up to 4 bytes (bytes past S are ignored).
+ *   lse          device fp32 [B, Hq, L] or NULL (as in psb_blockdiag_attn_fwd_lse_planned).
+ *   scale, enable_gqa, out  as in psb_blockdiag_attn_fwd.
+ * Every key tile of every row is visited: the cost is that of unmasked attention.  No
+ * workspace.  D must be 64 or 128.
+ */
+psb_status psb_blockdiag_dense_mask(const int32_t* doc_ids, int64_t B, int64_t S, int64_t seq_start, int64_t L,
+                                    uint8_t* mask_out, int64_t row_stride, void* stream);
+psb_status psb_masked_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* mask,
+                               int64_t mask_batch_stride, int64_t mask_row_stride, int64_t B, int64_t Hq,
+                               int64_t Hkv, int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                               const int64_t* kv_strides, float scale, int32_t enable_gqa, void* out, float* lse,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,9 @@ SIGNATURES = {
     "psb_validate_document_positions": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
     "psb_unpack_row_layout": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
     "psb_shard_kv_window_start": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "psb_blockdiag_dense_mask": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_i64, _vp]),
+    "psb_masked_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                     _c_i64, _vp, _vp, ctypes.c_float, _c_i32, _vp, _vp, _vp]),
     "psb_blockdiag_attn_fwd_window_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                                        _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, ctypes.c_float,
                                                        _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]),
@@ -461,3 +464,77 @@ def blockdiag_attn_bwd_window(q, k, v, out, dout, lse, doc_ids, workspace, seq_s
         _ptr(workspace), nbytes, _ptr(status), _vp(_stream(q))), "blockdiag_attn_bwd_window_planned")
     _window_status(status, "blockdiag_attn_bwd_window")
     return dq, dk, dv
+
+
+# ---- dense-mask path -------------------------------------------------------------------
+
+def blockdiag_dense_mask(doc_ids: torch.Tensor, seq_start: int = 0, L: int | None = None) -> torch.Tensor:
+    """The per-document causal mask of the query rows ``[seq_start, seq_start + L)``:
+    bool ``[B, L, S]`` (True = may attend), a view of rows padded to a multiple of 16
+    bytes (the layout :func:`masked_attn_fwd` reads without a copy)."""
+    _need_gpu(doc_ids)
+    ids = doc_ids.reshape(doc_ids.shape[0] if doc_ids.dim() > 1 else 1, -1)
+    ids = (ids if ids.dtype == torch.int32 else ids.to(torch.int32)).contiguous()
+    B, S = ids.shape
+    L = S - int(seq_start) if L is None else int(L)
+    stride = (S + 15) // 16 * 16
+    buf = torch.empty((B, L, stride), dtype=torch.bool, device=ids.device)
+    _check(load().psb_blockdiag_dense_mask(_ptr(ids), B, S, int(seq_start), L, _ptr(buf), stride,
+                                           _vp(_stream(ids))), "blockdiag_dense_mask")
+    return buf[:, :, :S]
+
+
+def _mask_operand(mask: torch.Tensor, B: int, L: int, S: int):
+    """(tensor, batch stride, row stride) the kernel can read: rows 4-byte aligned and
+    readable up to S rounded up to 4; anything else is copied into such a layout."""
+    m = mask
+    if m.dim() == 4:
+        if m.shape[1] != 1:
+            raise ValueError("a 4-D mask must be [B or 1, 1, L, S] (one mask for all heads)")
+        m = m[:, 0]
+    if m.dim() == 2:
+        m = m.unsqueeze(0)
+    if m.dim() != 3 or m.shape[1:] != (L, S) or m.shape[0] not in (1, B):
+        raise ValueError(f"mask must be [B or 1, L, S] = [{B}, {L}, {S}]")
+    if m.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("mask must be bool (True = may attend)")
+    sb = 0 if m.shape[0] == 1 else m.stride(0)
+    ss = m.stride(1)
+    S4 = (S + 3) // 4 * 4
+    end = m.storage_offset() + (m.shape[0] - 1) * sb + (L - 1) * ss + S4
+    ok = (m.stride(2) == 1 or S <= 1) and sb % 4 == 0 and ss % 4 == 0 and ss >= S4 and \
+        m.data_ptr() % 4 == 0 and end <= m.untyped_storage().nbytes()
+    if not ok:
+        stride = (S + 15) // 16 * 16
+        buf = torch.zeros((m.shape[0], L, stride), dtype=torch.bool, device=m.device)
+        buf[:, :, :S] = m != 0
+        m, sb, ss = buf, (0 if m.shape[0] == 1 else L * stride), stride
+    return m, sb, ss
+
+
+def masked_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor,
+                    scale: float | None = None, enable_gqa: bool = False, with_lse: bool = False):
+    """Attention under an explicit boolean mask ``[B or 1, L, S]`` (True = may attend,
+    the same for every head); rows without an allowed key give 0.  ``q [B, Hq, L, D]``,
+    ``k, v [B, Hkv, S, D]`` bf16 with a contiguous last dim.  Returns ``out`` or
+    ``(out, lse)``."""
+    _need_gpu(q, k, v, mask)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a 4-D bfloat16 tensor with a contiguous last dimension")
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k/v shape does not match q")
+    m, sb, ss = _mask_operand(mask, B, L, S)
+    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if with_lse else None
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    qs = (ctypes.c_int64 * 3)(*q.stride()[:3])
+    kvs = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    _check(load().psb_masked_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(m), sb, ss, B, Hq, Hkv, L, S, D, qs, kvs,
+                                      sc, 1 if enable_gqa else 0, _ptr(out), _ptr(lse), _vp(_stream(q))),
+           "masked_attn_fwd")
+    return (out, lse) if with_lse else out

@@ -59,6 +59,10 @@ struct AttnParams {
   const TileRecord* work;
   float* lse;     // [B, Hq, L] natural-log sum of exp(scale * q.k) per row, or null
   int32_t* status;  // PSB_DATA_KV_WINDOW when a row needs a key before kv_start, or null
+  // explicit-mask variant: mask[b * mask_sb + row * mask_ss + key] != 0 where row may see
+  // key; every row readable up to S rounded up to 4 bytes, 4-byte aligned
+  const uint8_t* mask;
+  int64_t mask_sb, mask_ss;
 };
 
 // the running row max is only moved (and O, l rescaled) when a tile's max exceeds
@@ -76,7 +80,10 @@ constexpr float kRescaleLog2 = 8.0f;
 //      of 64 bytes mod 256 puts those on distinct banks (D + 8 or D + 16 leaves 2- to
 //      4-way conflicts).
 
-template <int D, int NH>
+// DENSE: the explicit-mask variant (the dense-mask path next to the varlen kernels in
+// the blockdiag_cp package overview).  No plan: every row tile walks all keys [0, S) and
+// takes its mask bits from p.mask, prefetched one tile ahead.
+template <int D, int NH, bool DENSE>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int NR = kWaves / NH;
   constexpr int KS = D / 16;                              // k-steps of S^T = K Q^T
@@ -138,8 +145,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   // kv head on one XCD
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
     const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
-    const TileRecord& rec = p.work[rank];
-    const int32_t b = rec.b, rt = rec.rt;
+    int32_t b, rt, rec_lo, rec_hi;
+    const TileRecord* recp = nullptr;
+    if constexpr (DENSE) {
+      b = rank / p.ntile_row;
+      rt = rank % p.ntile_row;
+      rec_lo = 0;
+      rec_hi = p.S;
+    } else {
+      recp = &p.work[rank];
+      b = recp->b;
+      rt = recp->rt;
+      rec_lo = recp->lo;
+      rec_hi = recp->hi;
+    }
     // the records come from the caller's workspace: never index with a value that a
     // plan for this shape cannot have written
     if (b < 0 || b >= p.B || rt < 0 || rt >= p.ntile_row) continue;
@@ -151,8 +170,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const int32_t qpos = p.seq_start + row_local;
     // keys outside the delivered window are never loaded; a row that needs one (the
     // window does not reach back to its document start) is reported
-    const int32_t tlo = max(rec.lo, p.kv_start), thi = min(rec.hi, p.kv_end);
-    if (p.status != nullptr && tid == 0 && rec.hi > rec.lo && rec.lo < p.kv_start)
+    const int32_t tlo = max(rec_lo, p.kv_start), thi = min(rec_hi, p.kv_end);
+    if (!DENSE && p.status != nullptr && tid == 0 && rec_hi > rec_lo && rec_lo < p.kv_start)
       atomicOr(p.status, PSB_DATA_KV_WINDOW);
     __bf16* out_row = p.out + (((int64_t)b * p.Hq + hq) * p.L + row_local) * D;
 
@@ -193,22 +212,30 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       }
     };
     // ---- per-wave query block description ------------------------------------------
-    const int32_t w_lo = __builtin_amdgcn_readfirstlane(rec.blk_lo[wv / NH]);
-    const int32_t* docrow = p.doc + (int64_t)b * p.S;
-    const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
-    const bool valid = dq != PSB_PAD_DOC_ID;
-    const int32_t dprev = __shfl_up(dq, 1, kWave);
-    const bool flag = (lr == 0) || (dq != dprev);
-    const uint64_t fm = __ballot(flag) & 0xffffffffull;
-    const uint64_t upto = fm & ((2ull << lr) - 1ull);
-    const int rs = 63 - __clzll((long long)upto);             // last run start at or before my row
-    const int32_t wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
-    const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;       // my document's first position
-    // key k is allowed iff 0 <= k - start_q <= span (unsigned compare); padding rows: none
-    const uint32_t span = valid ? (uint32_t)(qpos - start_q) : 0u;
-    const int32_t kshift = valid ? start_q : 0x40000000;       // padding: k - kshift < 0 always
-    const bool single = __builtin_amdgcn_readfirstlane(
-        (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
+    int32_t w_lo = 0, wq0 = 0, kshift = 0;
+    uint32_t span = 0u;
+    bool single = false;
+    const uint8_t* mrow = nullptr;
+    if constexpr (DENSE) {
+      mrow = p.mask + (int64_t)b * p.mask_sb + (int64_t)row_local * p.mask_ss;
+    } else {
+      w_lo = __builtin_amdgcn_readfirstlane(recp->blk_lo[wv / NH]);
+      const int32_t* docrow = p.doc + (int64_t)b * p.S;
+      const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
+      const bool valid = dq != PSB_PAD_DOC_ID;
+      const int32_t dprev = __shfl_up(dq, 1, kWave);
+      const bool flag = (lr == 0) || (dq != dprev);
+      const uint64_t fm = __ballot(flag) & 0xffffffffull;
+      const uint64_t upto = fm & ((2ull << lr) - 1ull);
+      const int rs = 63 - __clzll((long long)upto);             // last run start at or before my row
+      wq0 = __builtin_amdgcn_readfirstlane(p.seq_start + blk * kRowsPerBlock);
+      const int32_t start_q = (rs == 0) ? w_lo : wq0 + rs;       // my document's first position
+      // key k is allowed iff 0 <= k - start_q <= span (unsigned compare); padding rows: none
+      span = valid ? (uint32_t)(qpos - start_q) : 0u;
+      kshift = valid ? start_q : 0x40000000;                     // padding: k - kshift < 0 always
+      single = __builtin_amdgcn_readfirstlane(
+          (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
+    }
 
     // ---- Q^T operand, resident for the whole tile loop (sign-flipped if scale < 0) -----
     bf16x8 qreg[KS];
@@ -272,8 +299,35 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_s_setprio(0);
     };
     // mask (unless both blocks lie inside one document's causal triangle) and row max
+    // explicit mask: the 32 bits this lane needs for one tile, 4 per 32-bit word (keys
+    // kt + 32 kb + 4 h + 8 g + {0..3} in word 4 kb + g); keys at or past S read as 0
+    auto load_mask = [&](int32_t kt, uint32_t (&mw)[8]) {
+      if constexpr (DENSE) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int32_t key0 = kt + 32 * (w >> 2) + 4 * h + 8 * (w & 3);
+          uint32_t x = 0u;
+          if (row_in && key0 < p.S) {
+            x = *(const uint32_t*)(mrow + key0);
+            if (p.S - key0 < 4) x &= (1u << (8 * (p.S - key0))) - 1u;
+          }
+          mw[w] = x;
+        }
+      }
+    };
+    auto apply_mask = [&](floatx16 (&s)[2], const uint32_t (&mw)[8]) {
+      if constexpr (DENSE) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t byte = (mw[4 * kb + (i >> 2)] >> (8 * (i & 3))) & 0xffu;
+            s[kb][i] = byte ? s[kb][i] : -INFINITY;
+          }
+      }
+    };
     auto mask_max = [&](int32_t kt, floatx16 (&s)[2]) {
-      const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
+      const bool full = DENSE || (single && kt >= w_lo && (kt + 63) <= wq0);
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -358,9 +412,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // Step t reads K(t), V(t) from sK0 / sV0 (t even) or sK1 / sV1 (t odd), loaded straight
     // into LDS during step t-1, and starts the loads of K(t+1), V(t+1) into the other pair.
     __syncthreads();  // the previous item no longer reads LDS
+    uint32_t mA[8], mB[8];  // explicit-mask words of the current / next tile (DENSE only)
     issue_k(sK0, tlo);
     issue_v(sV0, tlo);
-    auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext, const __bf16* vcur, __bf16* vnext) {
+    load_mask(tlo, mA);
+    auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext, const __bf16* vcur, __bf16* vnext,
+                    const uint32_t (&mcur)[8], uint32_t (&mnext)[8]) {
       const int32_t kt = tlo + t * kKeysPerTile;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t), V(t) loads landed
       __syncthreads();                                   // K(t), V(t) visible; other stages free
@@ -368,9 +425,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       if (more) {
         issue_k(knext, kt + kKeysPerTile);
         issue_v(vnext, kt + kKeysPerTile);
+        load_mask(kt + kKeysPerTile, mnext);
       }
       floatx16 st_s[2];
       qk(kcur, st_s);
+      apply_mask(st_s, mcur);
       float m_cand;
       const bool g = grows(mask_max(kt, st_s), m_cand);
       if (__builtin_amdgcn_readfirstlane(__ballot(g) != 0)) rescale(g, m_cand);
@@ -378,10 +437,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     };
     int32_t t = 0;
     for (; t + 1 < ntiles; t += 2) {
-      step(t, sK0, sK1, sV0, sV1);
-      step(t + 1, sK1, sK0, sV1, sV0);
+      step(t, sK0, sK1, sV0, sV1, mA, mB);
+      step(t + 1, sK1, sK0, sV1, sV0, mB, mA);
     }
-    if (t < ntiles) step(t, sK0, sK1, sV0, sV1);
+    if (t < ntiles) step(t, sK0, sK1, sV0, sV1, mA, mB);
 
     // ---- epilogue: O / l, padding rows (l == 0) -> 0 ----------------------------------
     const float l_tot = partner_sum(l_run);
@@ -408,12 +467,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 
 int heads_per_wg(int64_t group) { return (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1); }
 
-template <int D>
+template <int D, bool DENSE>
 hipError_t launch_attn(int nh, const AttnParams& prm, unsigned grid, hipStream_t s) {
   switch (nh) {
-    case 4: attn_fwd_kernel<D, 4><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
-    case 2: attn_fwd_kernel<D, 2><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
-    default: attn_fwd_kernel<D, 1><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
+    case 4: attn_fwd_kernel<D, 4, DENSE><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
+    case 2: attn_fwd_kernel<D, 2, DENSE><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
+    default: attn_fwd_kernel<D, 1, DENSE><<<dim3(grid), dim3(kThreads), 0, s>>>(prm); break;
   }
   return hipGetLastError();
 }
@@ -506,11 +565,13 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   prm.work = buf.work;
   prm.lse = lse;
   prm.status = status;
+  prm.mask = nullptr;
+  prm.mask_sb = prm.mask_ss = 0;
   // one workgroup per item: the dispatcher starts a new one whenever a slot frees,
   // which balances the longest-first order better than a fixed persistent split
   const int64_t grid = geo.grid;
-  const hipError_t e = (D == 128) ? launch_attn<128>((int)geo.nh, prm, (unsigned)grid, s)
-                                  : launch_attn<64>((int)geo.nh, prm, (unsigned)grid, s);
+  const hipError_t e = (D == 128) ? launch_attn<128, false>((int)geo.nh, prm, (unsigned)grid, s)
+                                  : launch_attn<64, false>((int)geo.nh, prm, (unsigned)grid, s);
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }
 
@@ -618,4 +679,69 @@ PSB_API psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const vo
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
   return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, kv_start, kv_len, scale,
                   geo, out, lse, const_cast<void*>(workspace), workspace_bytes, status_word, as_stream(stream));
+}
+
+PSB_API psb_status psb_masked_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                       int64_t mask_batch_stride, int64_t mask_row_stride, int64_t B, int64_t Hq,
+                                       int64_t Hkv, int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                       const int64_t* kv_strides, float scale, int32_t enable_gqa, void* out,
+                                       float* lse, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || L < 0 || S < 0 || D < 0) return PSB_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return PSB_ERR_UNSUPPORTED;
+  if (Hq > 0 && Hkv == 0) return PSB_ERR_SHAPE;
+  if (enable_gqa ? (Hkv > 0 && Hq % Hkv != 0) : (Hq != Hkv)) return PSB_ERR_SHAPE;
+  if (L >= INT32_MAX || S >= INT32_MAX - 64 || Hq >= INT32_MAX || B >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
+  if (!isfinite(scale)) return PSB_ERR_INVALID_ARG;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || mask == nullptr) return PSB_ERR_INVALID_ARG;
+  // the mask is read 4 bytes at a time: aligned rows, each readable up to S rounded up to 4
+  if ((reinterpret_cast<uintptr_t>(mask) & 3u) != 0) return PSB_ERR_INVALID_ARG;
+  if (mask_batch_stride < 0 || (mask_batch_stride % 4) != 0 || (mask_row_stride % 4) != 0 ||
+      mask_row_stride < (S + 3) / 4 * 4)
+    return PSB_ERR_SHAPE;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
+  const int64_t qs_def[3] = {Hq * L * D, L * D, D};
+  const int64_t kvs_def[3] = {Hkv * S * D, S * D, D};
+  const int64_t* qs = q_strides ? q_strides : qs_def;
+  const int64_t* kvs = kv_strides ? kv_strides : kvs_def;
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || kvs[i] < 0 || (qs[i] % 8) != 0 || (kvs[i] % 8) != 0) return PSB_ERR_SHAPE;
+  }
+  if (qs[2] < D || kvs[2] < D) return PSB_ERR_SHAPE;
+  if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PSB_ERR_INVALID_ARG;
+  AttnGeometry geo;
+  geo.group = Hq / Hkv;
+  geo.nh = heads_per_wg(geo.group);
+  geo.nr = kWaves / geo.nh;
+  geo.ntiles = schedule_ntiles(B, L, geo.nr);
+  geo.units = Hq / geo.nh;
+  geo.grid = geo.ntiles * geo.units;
+  if (geo.grid >= INT32_MAX) return PSB_ERR_SHAPE;
+  AttnParams prm;
+  prm.q = static_cast<const __bf16*>(q);
+  prm.k = static_cast<const __bf16*>(k);
+  prm.v = static_cast<const __bf16*>(v);
+  prm.doc = nullptr;
+  prm.out = static_cast<__bf16*>(out);
+  prm.q_sb = qs[0]; prm.q_sh = qs[1]; prm.q_ss = qs[2];
+  prm.kv_sb = kvs[0]; prm.kv_sh = kvs[1]; prm.kv_ss = kvs[2];
+  prm.kv_start = 0; prm.kv_end = (int32_t)S;
+  prm.B = (int32_t)B; prm.Hq = (int32_t)Hq; prm.Hkv = (int32_t)Hkv; prm.L = (int32_t)L; prm.S = (int32_t)S;
+  prm.seq_start = 0; prm.group = (int32_t)geo.group;
+  prm.nblk = (int32_t)schedule_nblk(L);
+  prm.ntile_row = (int32_t)(geo.ntiles / B);
+  prm.units = (int32_t)geo.units;
+  prm.sc = scale * kLog2e;
+  prm.items = geo.grid;
+  prm.work = nullptr;
+  prm.lse = lse;
+  prm.status = nullptr;
+  prm.mask = mask;
+  prm.mask_sb = mask_batch_stride;
+  prm.mask_ss = mask_row_stride;
+  hipStream_t s = as_stream(stream);
+  const hipError_t e = (D == 128) ? launch_attn<128, true>((int)geo.nh, prm, (unsigned)geo.grid, s)
+                                  : launch_attn<64, true>((int)geo.nh, prm, (unsigned)geo.grid, s);
+  return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }

@@ -286,6 +286,32 @@ __global__ void __launch_bounds__(kPosThreads) positions_kernel(const uint8_t* _
   if (__any(bad) && (threadIdx.x % kWave) == 0) atomicOr(status, PSB_DATA_BAD_POSITIONS);
 }
 
+// ---- dense per-document causal mask ----------------------------------------------------
+// One thread per 4 mask bytes: row i of the shard (global position seq_start + i) may
+// see key k iff doc[k] == doc[q], doc[q] is not padding and k <= q.  Bytes past S in a
+// padded row are written 0.
+__global__ void __launch_bounds__(256) dense_mask_kernel(const int32_t* __restrict__ doc_ids, int32_t S,
+                                                         int32_t seq_start, int32_t L, int64_t words_per_row,
+                                                         int64_t total_words, uint32_t* __restrict__ mask) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= total_words) return;
+  const int64_t row = w / words_per_row;            // b * L + i
+  const int32_t c = (int32_t)(w - row * words_per_row);
+  const int32_t b = (int32_t)(row / L), i = (int32_t)(row - (int64_t)b * L);
+  const int32_t* doc = doc_ids + (int64_t)b * S;
+  const int32_t qpos = seq_start + i;
+  const int32_t dq = doc[qpos];
+  uint32_t x = 0u;
+  if (dq != PSB_PAD_DOC_ID) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int32_t key = 4 * c + t;
+      if (key < S && key <= qpos && doc[key] == dq) x |= 1u << (8 * t);
+    }
+  }
+  mask[w] = x;
+}
+
 }  // namespace
 }  // namespace psb
 
@@ -372,6 +398,24 @@ PSB_API psb_status psb_unpack_row_layout(const int32_t* seq_lens, const int32_t*
   unpack_kernel<<<grid, dim3(kLensThreads), 0, as_stream(stream)>>>(seq_lens, seq_lens_padded, (int32_t)n_docs,
                                                                      (int32_t)seq_len, padding_mask_out,
                                                                      position_ids_out, status_word);
+  PSB_LAUNCH_CHECK();
+  return PSB_OK;
+}
+
+PSB_API psb_status psb_blockdiag_dense_mask(const int32_t* doc_ids, int64_t B, int64_t S, int64_t seq_start,
+                                            int64_t L, uint8_t* mask_out, int64_t row_stride, void* stream) {
+  if (B < 0 || S < 0 || L < 0 || seq_start < 0) return PSB_ERR_INVALID_ARG;
+  if (seq_start + L > S || S >= INT32_MAX || L >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (row_stride < S || (row_stride % 4) != 0) return PSB_ERR_SHAPE;
+  if (B == 0 || L == 0 || row_stride == 0) return PSB_OK;
+  if (doc_ids == nullptr || mask_out == nullptr || (reinterpret_cast<uintptr_t>(mask_out) & 3u) != 0)
+    return PSB_ERR_INVALID_ARG;
+  const int64_t wpr = row_stride / 4;
+  const int64_t total = B * L * wpr;
+  const int64_t blocks = ceil_div(total, 256);
+  if (blocks >= INT32_MAX) return PSB_ERR_SHAPE;
+  dense_mask_kernel<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(
+      doc_ids, (int32_t)S, (int32_t)seq_start, (int32_t)L, wpr, total, reinterpret_cast<uint32_t*>(mask_out));
   PSB_LAUNCH_CHECK();
   return PSB_OK;
 }
