@@ -58,7 +58,7 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(lay, q, k, v, budget_s: float = 10.0, max_passes: int = 4):
+def cpu_baseline(lay, q, k, v, budget_s: float = 10.0, max_passes: int = 40):
     import torch
     import oracle
     ids = [oracle.doc_ids_from_cu_seqlens(lay.cu_seqlens(b), lay.S)[0] for b in range(lay.B)]
