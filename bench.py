@@ -4,8 +4,8 @@
 
 One step = the whole device path over one batch of synthetic packed rows that
 is already resident in HBM:
-  doc_ids_from_cu_seqlens (per row) -> segment_cu_seqlens (per row)
-  -> tile schedule (plan) -> block-diagonal attention kernel.
+  step preparation for all rows (document ids, run boundaries, tile plan: one
+  kernel plus the plan's sort) -> block-diagonal attention kernel.
 The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
 
 Default workload: the packed LLM row (B=1, S=L=8192, Hq=32, Hkv=8, D=128,
@@ -14,7 +14,8 @@ Prints ONE JSON line.  The timed steps carry no events (an event record between
 two launches costs the queue a few microseconds).  `roofline` describes the
 attention kernel alone, timed with HIP events on the stream it is launched on
 around K back-to-back launches after the timed steps; `phase_ms` times the
-boundary calls and the plan the same way.  `traffic` is HBM bytes per launch
+preparation the same way, and for reference the separate per-row boundary calls
+and plan call that compute the same outputs.  `traffic` is HBM bytes per launch
 from the committed rocprofv3 counter runs, reported only while the kernel
 source is unchanged; `backward` times the training path's backward (dq, dk, dv)
 on the same workload; `cpu_baseline` times the CPU fp64 oracle on the host cores
@@ -226,6 +227,16 @@ def main():
                  ctypes.c_void_p(seg_cu[b].data_ptr()), ctypes.c_void_p(seg_n[b:].data_ptr()))
                 for b in range(B)]
     qp, kp, vp, dp, op, wp = P(q), P(k), P(v), P(doc_ids), P(out), P(ws)
+    # all rows' boundaries as one [B, N + 1] table (shorter rows repeat their last boundary)
+    n1 = max(c.numel() for c in cus)
+    cu_all = torch.stack([torch.cat([c, c[-1:].expand(n1 - c.numel())]) for c in cus]).to(torch.int32).contiguous()
+    cup, segp, segnp = P(cu_all), P(seg_cu), P(seg_n)
+
+    def prepare():
+        # the step's ids, run boundaries and plan for all rows: two launches
+        st = lib.psb_blockdiag_prepare(cup, n1, n1 - 1, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, dp, segp, segnp,
+                                       wp, ws_bytes, None, sptr)
+        assert st == 0, st
 
     def boundary():
         for cu_p, nd, ids_p, scu_p, sn_p in row_ptrs:
@@ -244,8 +255,7 @@ def main():
         assert st == 0, st
 
     def step():
-        boundary()
-        plan()
+        prepare()
         attention()
 
     for _ in range(args.warmup):
@@ -269,8 +279,9 @@ def main():
         return a0.elapsed_time(a1) / n
 
     attn_ms = timed(attention, args.steps)
-    phase_ms = {"boundary": round(timed(boundary, args.steps), 5), "plan": round(timed(plan, args.steps), 5),
-                "attention": round(attn_ms, 5)}
+    phase_ms = {"prepare": round(timed(prepare, args.steps), 5), "attention": round(attn_ms, 5),
+                "separate_calls": {"boundary_per_row": round(timed(boundary, args.steps), 5),
+                                   "plan": round(timed(plan, args.steps), 5)}}
     flops = lay.useful_flops()
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12

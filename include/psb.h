@@ -234,6 +234,30 @@ psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, const vo
                                           size_t workspace_bytes, int32_t* status_word, void* stream);
 
 /*
+ * The whole preparation of a step in two launches: document ids, run boundaries and the
+ * attention plan for B rows at once from their boundaries (glm5_next.cp page,
+ * doc_ids_from_cu_seqlens and segment_cu_seqlens; blockdiag_cp package overview,
+ * "varlen metadata precompute").  Outputs equal those of psb_doc_ids_from_cu_seqlens and
+ * psb_segment_cu_seqlens run on each row, and of psb_blockdiag_attn_plan on the ids.
+ *
+ *   cu_seqlens     device int32 [B][cu_row_stride]: row b's boundaries in its first
+ *                  n_docs + 1 entries.  Rows with fewer documents repeat their last
+ *                  boundary (zero-length documents take an id and cover nothing).
+ *   doc_ids_out    device int32 [B, S], contiguous (document i of a row gets id i + 1).
+ *   seg_cu_out     device int32 [B, S + 1], contiguous: row b's run boundaries
+ *                  [0, run starts..., S] in its first seg_n_out[b] + 1 entries.
+ *   seg_n_out      device int32 [B]: number of runs per row.
+ *   workspace      as for psb_blockdiag_attn_plan (may be NULL when L == 0 or Hq == 0).
+ *   status_word    device int32 or NULL: the bits of psb_doc_ids_from_cu_seqlens.
+ * Shape arguments and errors as in psb_blockdiag_attn_plan; B > 65535 returns
+ * PSB_ERR_SHAPE.
+ */
+psb_status psb_blockdiag_prepare(const int32_t* cu_seqlens, int64_t cu_row_stride, int64_t n_docs, int64_t B,
+                                 int64_t Hq, int64_t Hkv, int64_t L, int64_t S, int64_t D, int64_t seq_start,
+                                 int32_t enable_gqa, int32_t* doc_ids_out, int32_t* seg_cu_out, int32_t* seg_n_out,
+                                 void* workspace, size_t workspace_bytes, int32_t* status_word, void* stream);
+
+/*
  * psb_blockdiag_attn_fwd_planned for training: also writes, per query row, the
  * log-sum-exp the backward needs (the blockdiag_cp page keeps this path active
  * while backward recomputes checkpointed forwards).

@@ -25,7 +25,7 @@ Python face of ``libpsb.so`` (HIP kernels for gfx950, C ABI in include/psb.h):
 from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd, blockdiag_attn_fwd_lse,
                    bwd_workspace_size, doc_ids_from_cu_seqlens, doc_ids_from_seq_lens, load,
                    blockdiag_attn_bwd_window, blockdiag_attn_fwd_window, shard_kv_window_start,
-                   blockdiag_dense_mask, masked_attn_fwd,
+                   blockdiag_dense_mask, masked_attn_fwd, blockdiag_prepare,
                    segment_cu_seqlens, status_string, unpack_row_layout, unpack_row_layout_batch, validate_doc_ids,
                    validate_document_positions,
                    workspace_size)
@@ -39,7 +39,7 @@ __all__ = ["blockdiag_attention", "PackedState", "attach_packed_varlen_hooks", "
            "patched_sdpa", "PAD_DOC_ID", "PsbError", "blockdiag_attn_bwd", "blockdiag_attn_fwd", "blockdiag_attn_fwd_lse",
            "bwd_workspace_size", "doc_ids_from_cu_seqlens", "doc_ids_from_seq_lens", "load",
            "blockdiag_attn_bwd_window", "blockdiag_attn_fwd_window", "shard_kv_window_start",
-           "blockdiag_dense_mask", "masked_attn_fwd",
+           "blockdiag_dense_mask", "masked_attn_fwd", "blockdiag_prepare",
            "segment_cu_seqlens", "status_string", "unpack_row_layout", "unpack_row_layout_batch", "validate_doc_ids",
            "validate_document_positions",
            "workspace_size"]

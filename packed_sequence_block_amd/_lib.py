@@ -45,6 +45,8 @@ SIGNATURES = {
     "psb_validate_document_positions": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
     "psb_unpack_row_layout": (_c_i32, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
     "psb_shard_kv_window_start": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "psb_blockdiag_prepare": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                       _c_i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]),
     "psb_blockdiag_dense_mask": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_i64, _vp]),
     "psb_masked_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                      _c_i64, _vp, _vp, ctypes.c_float, _c_i32, _vp, _vp, _vp]),
@@ -538,3 +540,34 @@ def masked_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: tor
                                       sc, 1 if enable_gqa else 0, _ptr(out), _ptr(lse), _vp(_stream(q))),
            "masked_attn_fwd")
     return (out, lse) if with_lse else out
+
+
+def blockdiag_prepare(cu_seqlens: torch.Tensor, seq_len: int, Hq: int, Hkv: int, D: int, seq_start: int = 0,
+                      L: int | None = None, enable_gqa: bool = False, workspace: torch.Tensor | None = None,
+                      validate: bool = False):
+    """One step's preparation for B rows in two launches, from boundaries ``[B, N + 1]``
+    (rows with fewer documents repeat their last boundary): returns ``(doc_ids [B, S],
+    seg_cu [B, S + 1], seg_n [B], workspace)``; row b's run boundaries are
+    ``seg_cu[b, :seg_n[b] + 1]`` and the workspace holds the attention plan for
+    :func:`blockdiag_attn_fwd`-style planned calls with these shapes."""
+    _need_gpu(cu_seqlens)
+    cu = cu_seqlens if cu_seqlens.dim() == 2 else cu_seqlens.reshape(1, -1)
+    cu = (cu if cu.dtype == torch.int32 else cu.to(torch.int32)).contiguous()
+    B, n1 = cu.shape
+    S = int(seq_len)
+    L = S - int(seq_start) if L is None else int(L)
+    dev = cu.device
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    seg = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    need = workspace_size(B, Hq, Hkv, L, D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev) if validate else None
+    _check(load().psb_blockdiag_prepare(_ptr(cu), n1, n1 - 1, B, Hq, Hkv, L, S, D, int(seq_start),
+                                        1 if enable_gqa else 0, _ptr(ids), _ptr(seg), _ptr(n), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(status),
+                                        _vp(_stream(cu))), "blockdiag_prepare")
+    if validate and int(status.item()) != 0:
+        raise ValueError(f"cu_seqlens invalid (status bits {int(status.item())})")
+    return ids, seg, n, workspace

@@ -588,6 +588,34 @@ PSB_API size_t psb_blockdiag_attn_fwd_workspace_size(int64_t B, int64_t Hq, int6
   return (size_t)schedule_bytes(B, L, nr);
 }
 
+PSB_API psb_status psb_blockdiag_prepare(const int32_t* cu_seqlens, int64_t cu_row_stride, int64_t n_docs,
+                                         int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S, int64_t D,
+                                         int64_t seq_start, int32_t enable_gqa, int32_t* doc_ids_out,
+                                         int32_t* seg_cu_out, int32_t* seg_n_out, void* workspace,
+                                         size_t workspace_bytes, int32_t* status_word, void* stream) {
+  AttnGeometry geo;
+  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  if (st != PSB_OK) return st;
+  if (n_docs < 0 || cu_row_stride < n_docs + 1) return PSB_ERR_SHAPE;
+  if (B == 0) return PSB_OK;
+  if (B > 65535 || n_docs >= INT32_MAX) return PSB_ERR_SHAPE;
+  if (cu_seqlens == nullptr || seg_cu_out == nullptr || seg_n_out == nullptr || (S > 0 && doc_ids_out == nullptr))
+    return PSB_ERR_INVALID_ARG;
+  const bool plan = Hq > 0 && L > 0;
+  if (plan) {
+    if (workspace == nullptr || !aligned16(workspace)) return PSB_ERR_INVALID_ARG;
+    if (workspace_bytes < (size_t)schedule_bytes(B, L, geo.nr)) return PSB_ERR_CAPACITY;
+  }
+  const int64_t id_chunks = (S + 255) / 256;
+  if (B * id_chunks + B * schedule_nblk(L) + B >= INT32_MAX) return PSB_ERR_SHAPE;
+  ScheduleBuffers buf = {nullptr, nullptr, nullptr};
+  if (plan) buf = schedule_carve(workspace, B, L, geo.nr);
+  const hipError_t e = launch_prepare(cu_seqlens, cu_row_stride, (int32_t)n_docs, (int32_t)B, (int32_t)S,
+                                      plan ? (int32_t)L : 0, (int32_t)seq_start, (int32_t)geo.nr, doc_ids_out,
+                                      seg_cu_out, seg_n_out, buf, status_word, as_stream(stream));
+  return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
+}
+
 PSB_API psb_status psb_blockdiag_attn_plan(const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
                                            int64_t S, int64_t D, int64_t seq_start, int32_t enable_gqa,
                                            void* workspace, size_t workspace_bytes, void* stream) {

@@ -18,16 +18,6 @@ namespace {
 // Threads below n_docs also check that the boundaries are non-decreasing.
 constexpr int kCuLds = 4096;
 
-__device__ inline int32_t last_le(const int32_t* c, int32_t n, int32_t p) {
-  // largest i in [0, n) with c[i] <= p, or -1
-  int32_t lo = 0, hi = n;  // search in [lo, hi)
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (c[mid] <= p) lo = mid + 1; else hi = mid;
-  }
-  return lo - 1;
-}
-
 __global__ void __launch_bounds__(256) doc_ids_kernel(const int32_t* __restrict__ cu, int32_t n_docs,
                                                       int32_t seq_len, int32_t* __restrict__ ids,
                                                       int32_t* __restrict__ status) {

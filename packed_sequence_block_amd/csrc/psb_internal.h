@@ -23,4 +23,14 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Wavefront size of gfx950.
 constexpr int kWave = 64;
 
+// Largest i in [0, n) with c[i] <= p, or -1 (c non-decreasing).
+__device__ inline int32_t last_le(const int32_t* c, int32_t n, int32_t p) {
+  int32_t lo = 0, hi = n;  // search in [lo, hi)
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (c[mid] <= p) lo = mid + 1; else hi = mid;
+  }
+  return lo - 1;
+}
+
 }  // namespace psb

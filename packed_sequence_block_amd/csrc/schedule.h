@@ -50,6 +50,12 @@ inline ScheduleBuffers schedule_carve(void* ws, int64_t B, int64_t L, int64_t nr
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
                            int32_t nr, const ScheduleBuffers& buf, hipStream_t stream);
 
+// Document ids, run boundaries and the plan above for B rows at once, from boundaries
+// cu [B][n_docs + 1] (row stride cu_stride): two launches.
+hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
+                          int32_t seq_start, int32_t nr, int32_t* ids, int32_t* seg_cu, int32_t* seg_n,
+                          const ScheduleBuffers& buf, int32_t* status, hipStream_t stream);
+
 // Backward key side: tiles of kKeyTile keys of the window [kv_start, kv_start + kv_len),
 // each with the local query rows that see its keys, ordered by row-range length
 // (longest first).  The tables are sized for the whole row (kv_len <= S).

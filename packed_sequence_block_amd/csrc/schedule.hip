@@ -185,6 +185,121 @@ __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restric
   }
 }
 
+// ---- one-launch preparation from batched boundaries --------------------------------------
+// The per-step work before attention, for B rows at once from their boundaries cu
+// [B][n_docs + 1] (a row with fewer documents repeats its last boundary: zero-length
+// documents change neither ids nor segments nor ranges).  Three kinds of workgroups in
+// one grid:
+//   * ids:      one thread per position, the doc_ids_from_cu_seqlens rule (boundaries
+//               staged in LDS when they fit), plus the boundary checks;
+//   * ranges:   one wave per 32-row query block: the first valid row q_f is
+//               max(first row, cu[0]) and the last q_l = min(end, cu[n]) - 1; the range is
+//               [start of q_f's document, q_l + 1) — what block_range_kernel finds from the
+//               ids, computed from the boundaries directly;
+//   * segments: one workgroup per row: the run boundaries of the ids the row will hold,
+//               from the boundaries (cu[0] when a non-empty document follows leading
+//               padding, and the end of every non-empty document short of S).
+constexpr int kPrepThreads = 256;
+
+__global__ void __launch_bounds__(kPrepThreads) prepare_kernel(
+    const int32_t* __restrict__ cu_all, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
+    int32_t seq_start, int32_t nblk, int32_t id_chunks, int32_t range_groups, int32_t* __restrict__ ids,
+    int32_t* __restrict__ seg_cu, int32_t* __restrict__ seg_n, int32_t* __restrict__ blk_lo,
+    int32_t* __restrict__ blk_hi, int32_t* __restrict__ status) {
+  constexpr int kCuStage = 4096;
+  __shared__ int32_t scu[kCuStage];
+  __shared__ int32_t wsum[kPrepThreads / kWave];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int64_t id_blocks = (int64_t)B * id_chunks;
+  const int64_t bx = blockIdx.x;
+  if (bx < id_blocks) {
+    const int32_t b = (int32_t)(bx / id_chunks), chunk = (int32_t)(bx % id_chunks);
+    const int32_t* cu = cu_all + (int64_t)b * cu_stride;
+    if (status != nullptr && chunk == 0) {
+      int32_t bits = 0;
+      for (int32_t j = tid; j < n_docs; j += kPrepThreads)
+        if (cu[j + 1] < cu[j]) bits |= PSB_DATA_CU_NOT_MONOTONE;
+      if (tid == 0 && (cu[0] < 0 || cu[n_docs] > S)) bits |= PSB_DATA_CU_OUT_OF_RANGE;
+      if (bits) atomicOr(status, bits);
+    }
+    const int32_t p = chunk * kPrepThreads + tid;
+    int32_t i;
+    if (n_docs + 1 <= kCuStage) {  // uniform over the grid
+      for (int32_t j = tid; j <= n_docs; j += kPrepThreads) scu[j] = cu[j];
+      __syncthreads();
+      if (p >= S) return;
+      i = last_le(scu, n_docs + 1, p);
+    } else {
+      if (p >= S) return;
+      i = last_le(cu, n_docs + 1, p);
+    }
+    ids[(int64_t)b * S + p] = (i >= 0 && i < n_docs) ? i + 1 : PSB_PAD_DOC_ID;
+    return;
+  }
+  if (bx < id_blocks + range_groups) {
+    const int64_t w = (bx - id_blocks) * (kPrepThreads / kWave) + wv;
+    if (w >= (int64_t)B * nblk) return;
+    const int32_t b = (int32_t)(w / nblk), blk = (int32_t)(w % nblk);
+    const int32_t* cu = cu_all + (int64_t)b * cu_stride;
+    const int32_t c0 = cu[0], cn = cu[n_docs];
+    const int32_t r0 = seq_start + blk * kRowsPerBlock;
+    const int32_t r1 = seq_start + min(L, (blk + 1) * kRowsPerBlock);
+    const int32_t qf = max(r0, c0), ql = min(r1, cn) - 1;
+    int32_t lo = 0, hi = 0;
+    if (qf <= ql) {
+      lo = cu[max(last_le(cu, n_docs + 1, qf), 0)];  // >= 0 for valid boundaries
+      hi = ql + 1;
+    }
+    if (lane == 0) {
+      blk_lo[w] = lo;
+      blk_hi[w] = hi;
+    }
+    return;
+  }
+  // segments of row b
+  const int32_t b = (int32_t)(bx - id_blocks - range_groups);
+  if (b >= B) return;
+  const int32_t* cu = cu_all + (int64_t)b * cu_stride;
+  int32_t* out = seg_cu + (int64_t)b * (S + 1);
+  const int32_t c0 = cu[0], cn = cu[n_docs];
+  if (tid == 0) {
+    carry = 0;
+    out[0] = 0;
+  }
+  __syncthreads();
+  for (int32_t j0 = 0; j0 <= n_docs; j0 += kPrepThreads) {
+    const int32_t j = j0 + tid;
+    bool f = false;
+    int32_t val = 0;
+    if (j <= n_docs) {
+      val = cu[j];
+      f = (j == 0) ? (c0 > 0 && cn > c0) : (val > cu[j - 1] && val < S);
+    }
+    const uint64_t m = __ballot(f);
+    const int32_t below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wv] = __popcll(m);
+    __syncthreads();
+    int32_t base = carry;
+    for (int w = 0; w < wv; ++w) base += wsum[w];
+    // valid boundaries flag at most S - 1 strictly increasing values; the bound keeps
+    // invalid ones (reported by the ids workgroups) inside the row
+    if (f && base + below < S - 1) out[1 + base + below] = val;
+    __syncthreads();
+    if (tid == 0) carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (S > 0) {
+      const int32_t r = min(carry, S - 1);
+      out[1 + r] = S;
+      seg_n[b] = 1 + r;
+    } else {
+      seg_n[b] = 0;
+    }
+  }
+}
+
 // ---- key window of a query shard ----------------------------------------------------
 // One wave per batch row: the first non-padding row of the shard (64 rows per ballot),
 // then the start of its document by the same 64-way search as block_range_kernel.
@@ -283,3 +398,26 @@ PSB_API psb_status psb_shard_kv_window_start(const int32_t* doc_ids, int64_t B, 
   PSB_LAUNCH_CHECK();
   return PSB_OK;
 }
+
+namespace psb {
+
+hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
+                          int32_t seq_start, int32_t nr, int32_t* ids, int32_t* seg_cu, int32_t* seg_n,
+                          const ScheduleBuffers& buf, int32_t* status, hipStream_t stream) {
+  const int32_t nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int32_t id_chunks = (S + kPrepThreads - 1) / kPrepThreads;
+  const int64_t waves_per_wg = kPrepThreads / kWave;
+  const int32_t range_groups = (int32_t)(((int64_t)B * nblk + waves_per_wg - 1) / waves_per_wg);
+  const int64_t grid = (int64_t)B * id_chunks + range_groups + B;
+  prepare_kernel<<<dim3((unsigned)grid), dim3(kPrepThreads), 0, stream>>>(
+      cu, cu_stride, n_docs, B, S, L, seq_start, nblk, id_chunks, range_groups, ids, seg_cu, seg_n, buf.blk_lo,
+      buf.blk_hi, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nblk == 0) return e;
+  const int32_t ntile_row = (nblk + nr - 1) / nr;
+  tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
+                                                                buf.work);
+  return hipGetLastError();
+}
+
+}  // namespace psb

@@ -64,13 +64,17 @@ def run_plan(lib, ids_np, Hq, Hkv, L, seq_start, D=128):
 
 
 def check_plan(lib, ids_np, Hq, Hkv, L, seq_start):
+    check_plan_words(run_plan(lib, ids_np, Hq, Hkv, L, seq_start), ids_np, Hq, Hkv, L, seq_start)
+
+
+def check_plan_words(words, ids_np, Hq, Hkv, L, seq_start):
+    """The plan tables in a workspace (as int32 words) against the definition."""
     B = ids_np.shape[0]
     group = Hq // Hkv
     nh = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
     nr = 4 // nh
     nblk = (L + ROWS - 1) // ROWS
     ntile_row = (nblk + nr - 1) // nr
-    words = run_plan(lib, ids_np, Hq, Hkv, L, seq_start)
     lo, hi = ref_blocks(ids_np, L, seq_start)
     off = pad256(4 * B * nblk) // 4
     got_lo = words[:B * nblk].reshape(B, nblk)
