@@ -174,6 +174,83 @@ def dense_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
             "visited_tflops": round(visited / (attn_ms * 1e-3) / 1e12, 3)}
 
 
+def variants_leg(psb, lay, stream, steps, timed):
+    """The boundary variants on the workload's rows: ids from a -1000-padded length table,
+    the row layout (padding mask, positions) from real / padded lengths (each document
+    padded up to a multiple of 8 tokens), and the document-position check on that layout."""
+    import torch
+    B, S = lay.B, lay.S
+    n = max(len(r) for r in lay.doc_lens)
+    real = torch.full((B, n), -1000, dtype=torch.int32)
+    padded = torch.full((B, n), -1000, dtype=torch.int32)
+    for b, row in enumerate(lay.doc_lens):
+        left = S
+        for j, d in enumerate(row):
+            q = min((int(d) + 7) // 8 * 8, left)
+            real[b, j], padded[b, j] = min(int(d), q), q
+            left -= q
+    real, padded = real.to("cuda"), padded.to("cuda")
+    ids = psb.doc_ids_from_seq_lens(real, S)
+    mask, pos = psb.unpack_row_layout(real, padded, S)
+    keep = (~mask).to(torch.uint8)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib = psb.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def f_ids():
+        assert lib.psb_doc_ids_from_seq_lens(P(real), B, n, S, -1000, P(ids), None, sptr) == 0
+
+    def f_unpack():
+        assert lib.psb_unpack_row_layout(P(real), P(padded), B, n, S, P(mask), P(pos), None, sptr) == 0
+
+    def f_check():
+        assert lib.psb_validate_document_positions(P(keep), P(pos), B, S, P(status), sptr) == 0
+
+    for f in (f_ids, f_unpack, f_check):
+        f()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "unpacked layout breaks the document rule"
+    return {"what": "boundary variants on the workload's rows (ms per call)",
+            "doc_ids_from_seq_lens": round(timed(f_ids, steps), 5),
+            "unpack_row_layout": round(timed(f_unpack, steps), 5),
+            "validate_document_positions": round(timed(f_check, steps), 5)}
+
+
+def dropin_leg(psb, lay, q, k, v, doc_ids, steps):
+    """The SDPA drop-in as a model would call it (module code calls the stock
+    scaled_dot_product_attention while a packed step is armed): forward, and forward +
+    backward through autograd, wall-clock per call including the custom-op dispatch."""
+    import torch
+    import torch.nn.functional as F
+    g = torch.Generator().manual_seed(78)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(q.device)
+    qg, kg, vg = (t.detach().clone().requires_grad_(True) for t in (q, k, v))
+    n = max(3, steps // 5)
+
+    def fwd():
+        with torch.no_grad(), psb.packed_documents(doc_ids, lay.seq_start), psb.patched_sdpa():
+            return F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=lay.enable_gqa)
+
+    def fwd_bwd():
+        with psb.packed_documents(doc_ids, lay.seq_start), psb.patched_sdpa():
+            out = F.scaled_dot_product_attention(qg, kg, vg, is_causal=True, enable_gqa=lay.enable_gqa)
+        out.backward(dout)
+
+    res = {}
+    for name, fn in (("forward_ms", fwd), ("forward_backward_ms", fwd_bwd)):
+        for _ in range(3):  # the first backward also starts autograd's device thread
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = round((time.perf_counter() - t0) * 1e3 / n, 5)
+    res["what"] = "F.scaled_dot_product_attention swapped for the packed path (custom ops), wall clock"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +378,8 @@ def main():
     }
     if not args.no_dense:
         rec["dense_mask"] = dense_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
+    rec["boundary_variants"] = variants_leg(psb, lay, stream, args.steps, timed)
+    rec["drop_in"] = dropin_leg(psb, lay, q, k, v, doc_ids, args.steps)
     rec["kv_window"] = window_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
     if not args.no_backward:
         rec["backward"] = backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)

@@ -67,6 +67,7 @@ def _bwd_fake(q, k, v, out, dout, lse, doc_ids, workspace, seq_start, scale, ena
 
 
 def _setup_context(ctx, inputs, output):
+    ctx.set_materialize_grads(False)  # lse and workspace get no gradient: no zero tensors for them
     q, k, v, doc_ids, seq_start, scale, enable_gqa = inputs
     out, lse, ws = output
     ctx.save_for_backward(q, k, v, out, lse, doc_ids, ws)
@@ -75,6 +76,8 @@ def _setup_context(ctx, inputs, output):
 
 def _backward(ctx, dout, dlse, dws):
     q, k, v, out, lse, doc_ids, ws = ctx.saved_tensors
+    if dout is None:  # the output was not used by the loss
+        return None, None, None, None, None, None, None
     seq_start, scale, enable_gqa = ctx.args
     dq, dk, dv = blockdiag_attn_bwd_op(q, k, v, out, dout, lse, doc_ids, ws, seq_start, scale, enable_gqa)
     return dq, dk, dv, None, None, None, None
