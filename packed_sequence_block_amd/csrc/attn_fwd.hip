@@ -188,13 +188,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     }
     const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
 
-    // ---- tile loads: K global -> LDS directly; V global -> VGPRs -> V^T in LDS ----------
+    // ---- tile loads: K and V global -> LDS directly (buffer_load ... lds) -------------------
+    // A resource with num_records 0 turns every lane of a load into a zero fill with no
+    // memory access; the step after the last tile issues such loads into the free stage.
     const __bf16* kbase = p.k + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
     const __bf16* vbase = p.v + (int64_t)b * p.kv_sb + (int64_t)g * p.kv_sh;
+    auto rsrc_k = [&](int32_t kt, bool on) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
+                                               on ? min(thi - kt, kKeysPerTile) * row_bytes : 0, kBufferFlags);
+    };
+    auto rsrc_v = [&](int32_t kt, bool on) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
+                                               on ? min(thi - kt, kKeysPerTile) * row_bytes : 0, kBufferFlags);
+    };
+    constexpr int KFULL = KSEGS / kWaves;  // K segments every wave loads
     auto issue_k = [&](__bf16* kbuf, int32_t kt) {
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
-          min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rk = rsrc_k(kt, true);
 #pragma unroll
       for (int j = 0; j < KSEG_ITERS; ++j) {
         const int seg = j * kWaves + wv;
@@ -202,26 +211,49 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       }
     };
     auto issue_v = [&](__bf16* vbuf, int32_t kt) {
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + (int64_t)(kt - p.kv_start) * p.kv_ss), (short)0,
-          min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rv = rsrc_v(kt, true);
 #pragma unroll
       for (int j = 0; j < VSEG_ITERS; ++j) {
         const int seg = j * kWaves + wv;
         if (VSEGS % kWaves == 0 || seg < VSEGS) buffer_load_lds16(rv, vbuf + seg * 512, voff[j]);
       }
     };
-    // ---- per-wave query block description ------------------------------------------
-    int32_t w_lo = 0, wq0 = 0, kshift = 0;
-    uint32_t span = 0u;
-    bool single = false;
+    // ---- this item's Q^T operand, document id and block start ---------------------------
+    // All loads that depend only on the record are issued before the tile-0 loads, so that
+    // waiting for them (vmcnt counts in issue order) does not wait for tile 0 as well.
+    bf16x8 qreg[KS];
+    {
+      const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (row_in) {
+          qreg[ks] = *(const bf16x8*)(qsrc + 16 * ks + 8 * h);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) qreg[ks][t] = (__bf16)0.f;
+        }
+      }
+    }
+    int32_t w_lo = 0, dq = PSB_PAD_DOC_ID;
     const uint8_t* mrow = nullptr;
     if constexpr (DENSE) {
       mrow = p.mask + (int64_t)b * p.mask_sb + (int64_t)row_local * p.mask_ss;
     } else {
-      w_lo = __builtin_amdgcn_readfirstlane(recp->blk_lo[wv / NH]);
-      const int32_t* docrow = p.doc + (int64_t)b * p.S;
-      const int32_t dq = row_in ? docrow[qpos] : PSB_PAD_DOC_ID;
+      w_lo = recp->blk_lo[wv / NH];
+      if (row_in) dq = p.doc[(int64_t)b * p.S + qpos];
+    }
+    // the previous item no longer reads LDS (its operands were consumed by its MFMAs); a
+    // plain barrier leaves the loads above in flight
+    __builtin_amdgcn_s_barrier();
+    issue_k(sK0, tlo);
+    issue_v(sV0, tlo);
+
+    // ---- per-wave query block description ------------------------------------------
+    int32_t wq0 = 0, kshift = 0;
+    uint32_t span = 0u;
+    bool single = false;
+    if constexpr (!DENSE) {
+      w_lo = __builtin_amdgcn_readfirstlane(w_lo);
       const bool valid = dq != PSB_PAD_DOC_ID;
       const int32_t dprev = __shfl_up(dq, 1, kWave);
       const bool flag = (lr == 0) || (dq != dprev);
@@ -236,24 +268,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       single = __builtin_amdgcn_readfirstlane(
           (fm == 1ull) && ((__ballot(valid) & 0xffffffffull) == 0xffffffffull));
     }
-
-    // ---- Q^T operand, resident for the whole tile loop (sign-flipped if scale < 0) -----
-    bf16x8 qreg[KS];
-    {
-      const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
+    // a negative scale is folded into Q (sign flip) so the loop can use |scale|
+    if (neg) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (row_in) {
-          qreg[ks] = *(const bf16x8*)(qsrc + 16 * ks + 8 * h);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) qreg[ks][t] = (__bf16)0.f;
-        }
-        if (neg) {
-          short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
-          bits ^= (short)0x8000;
-          qreg[ks] = __builtin_bit_cast(bf16x8, bits);
-        }
+        short8v bits = __builtin_bit_cast(short8v, qreg[ks]);
+        bits ^= (short)0x8000;
+        qreg[ks] = __builtin_bit_cast(bf16x8, bits);
       }
     }
 
@@ -267,7 +288,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // Both MFMA phases (qk and softmax_pv) run at raised wave priority: the other wave on
     // the SIMD is then usually in its VALU / memory phases, and the arbiter lets the MFMA
     // issue first instead of leaving the matrix pipe idle.
-    auto qk = [&](const __bf16* kbuf, floatx16 (&s)[2]) {
+    static_assert(VSEGS % kWaves == 0, "V segments split evenly over the waves");
+    auto qk = [&](const __bf16* kbuf, floatx16 (&s)[2], __amdgpu_buffer_rsrc_t rkn, __bf16* knext,
+                  __amdgpu_buffer_rsrc_t rvn, __bf16* vnext) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       const __bf16* kp = kbuf + k_rd;
@@ -287,12 +310,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], ks ? s[0] : zero16, 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], ks ? s[1] : zero16, 0, 0, 0);
+        // next tile's loads, one segment per k-step: K first, then V
+        if (ks < KFULL) {
+          buffer_load_lds16(rkn, knext + (ks * kWaves + wv) * 512, koff[ks]);
+        } else if (ks - KFULL < VSEG_ITERS) {
+          buffer_load_lds16(rvn, vnext + ((ks - KFULL) * kWaves + wv) * 512, voff[ks - KFULL]);
+        }
       }
-      // keep 2*AH operand reads in flight: LDS latency under load is several MFMA slots
+#pragma unroll
+      for (int j = KS - KFULL; j < VSEG_ITERS; ++j) buffer_load_lds16(rvn, vnext + (j * kWaves + wv) * 512, voff[j]);
+      // keep 2*AH operand reads in flight; one load of the next tile after every k-step
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if ((i & 1) && (i >> 1) < KFULL + VSEG_ITERS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         if (i + 2 * AH < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -411,10 +443,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // ---- tile loop ----------------------------------------------------------------------
     // Step t reads K(t), V(t) from sK0 / sV0 (t even) or sK1 / sV1 (t odd), loaded straight
     // into LDS during step t-1, and starts the loads of K(t+1), V(t+1) into the other pair.
-    __syncthreads();  // the previous item no longer reads LDS
+    // Those loads are spread over the K Q^T MFMAs, one 1 KiB segment per k-step: issued as
+    // one burst at the top of the step they queued behind each other and held the LDS and
+    // the waves longer (5-8% of the kernel time on the D = 128 workloads).
     uint32_t mA[8], mB[8];  // explicit-mask words of the current / next tile (DENSE only)
-    issue_k(sK0, tlo);
-    issue_v(sV0, tlo);
     load_mask(tlo, mA);
     auto step = [&](int32_t t, const __bf16* kcur, __bf16* knext, const __bf16* vcur, __bf16* vnext,
                     const uint32_t (&mcur)[8], uint32_t (&mnext)[8]) {
@@ -422,13 +454,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K(t), V(t) loads landed
       __syncthreads();                                   // K(t), V(t) visible; other stages free
       const bool more = t + 1 < ntiles;
-      if (more) {
-        issue_k(knext, kt + kKeysPerTile);
-        issue_v(vnext, kt + kKeysPerTile);
-        load_mask(kt + kKeysPerTile, mnext);
+      const __amdgpu_buffer_rsrc_t rkn = rsrc_k(kt + kKeysPerTile, more);
+      const __amdgpu_buffer_rsrc_t rvn = rsrc_v(kt + kKeysPerTile, more);
+      if constexpr (KSEGS % kWaves != 0) {  // the segments left over after KFULL rounds
+        const int seg = KFULL * kWaves + wv;
+        if (more && seg < KSEGS) buffer_load_lds16(rkn, knext + seg * 512, koff[KFULL]);
       }
       floatx16 st_s[2];
-      qk(kcur, st_s);
+      qk(kcur, st_s, rkn, knext, rvn, vnext);
+      if (more) load_mask(kt + kKeysPerTile, mnext);
       apply_mask(st_s, mcur);
       float m_cand;
       const bool g = grows(mask_max(kt, st_s), m_cand);
