@@ -432,41 +432,75 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     const int32_t nsteps_h = (wg_hi > wg_lo) ? (wg_hi - wg_lo + kRowsPerStep - 1) / kRowsPerStep : 0;
     float pend_l = 0.f, pend_d = 0.f;
     const int32_t nsteps = nsteps_h * p.group;
-    auto issue = [&](int32_t st, __bf16* qb, __bf16* ob, int stage) {
+    // buffer resources of step st's Q and dO rows; a step past the last gets zero records,
+    // so its loads become zero fills of the free stage with no memory access
+    struct StepRsrc { __amdgpu_buffer_rsrc_t q, o; };
+    auto step_rsrc = [&](int32_t st) {
+      const bool on = st < nsteps;
+      const int32_t sst = on ? st : 0;
+      const int32_t hh = sst / nsteps_h, rr = wg_lo + (sst % nsteps_h) * kRowsPerStep;
+      const int32_t hq = g * p.group + hh;
+      const int64_t base = ((int64_t)b * p.Hq + hq) * p.L + rr;
+      const int32_t nrows = on ? min(kRowsPerStep, p.L - rr) : 0;
+      StepRsrc r;
+      r.q = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + base * D), (short)0, nrows * row_bytes, kBufferFlags);
+      r.o = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + base * D), (short)0, nrows * row_bytes, kBufferFlags);
+      return r;
+    };
+    // segments every wave loads (QFULL rounds) and the rest (waves wv < QSEGS % waves)
+    constexpr int QFULL = QSEGS / kBwdWaves;
+    // at D = 64 (32-row steps, 8 MFMAs) the loads need the whole step to land: issued at
+    // the top as one burst there, spread over the first MFMA loop at D = 128
+    constexpr bool SPREAD = D == 128;
+    auto issue_seg = [&](const StepRsrc& r, __bf16* qb, __bf16* ob, int j) {
+      const int seg = j * kBwdWaves + wv;
+      buffer_load_lds16(r.q, qb + seg * 512, qoff[j]);
+      buffer_load_lds16(r.o, ob + seg * 512, qoff[j]);
+    };
+    auto issue_rest = [&](const StepRsrc& r, __bf16* qb, __bf16* ob) {
+      if constexpr (QSEGS % kBwdWaves != 0) {
+        if (QFULL * kBwdWaves + wv < QSEGS) issue_seg(r, qb, ob, QFULL);
+      }
+    };
+    // the step's row lse / delta go to registers now and to LDS at the step's start,
+    // after the wait that the tile loads need anyway
+    auto issue_rows = [&](int32_t st) {
       const int32_t hh = st / nsteps_h, rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
       const int32_t hq = g * p.group + hh;
       const int64_t base = ((int64_t)b * p.Hq + hq) * p.L + rr;
       const int32_t nrows = min(kRowsPerStep, p.L - rr);
-      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.q + base * D), (short)0, nrows * row_bytes, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.dout + base * D), (short)0, nrows * row_bytes, kBufferFlags);
-#pragma unroll
-      for (int j = 0; j < QSEG_ITERS; ++j) {
-        const int seg = j * kBwdWaves + wv;
-        if (QSEGS % kBwdWaves == 0 || seg < QSEGS) {
-          buffer_load_lds16(rq, qb + seg * 512, qoff[j]);
-          buffer_load_lds16(ro, ob + seg * 512, qoff[j]);
-        }
-      }
-      // this step's row lse / delta go to registers now and to LDS at the step's start,
-      // after the wait that the loads above need anyway
       if (tid < kRowsPerStep) {
         const bool in = tid < nrows;
         const float l = in ? p.lse[base + tid] : 0.f;
         pend_l = (l == -INFINITY) ? 0.f : l * kLog2e;  // rows without keys: P is masked to 0
         pend_d = in ? p.delta[base + tid] : 0.f;
       }
-      (void)stage;
+    };
+    auto issue = [&](int32_t st, __bf16* qb, __bf16* ob) {
+      const StepRsrc r = step_rsrc(st);
+#pragma unroll
+      for (int j = 0; j < QFULL; ++j) issue_seg(r, qb, ob, j);
+      issue_rest(r, qb, ob);
+      issue_rows(st);
     };
 
     // one step: kRowsPerStep rows as NHALF independent 32-row halves, so the MFMAs of one
     // half can run while the other's probabilities are computed
     constexpr int NHALF = kRowsPerStep / 32;
-    auto compute = [&](int32_t st, const __bf16* qb, const __bf16* ob, int stage) {
+    // the next step's full-round segments are issued inside the first MFMA loop, one every
+    // KS / QFULL k-steps, alternating Q and dO (a wave with nothing to compute issues them
+    // at once)
+    auto compute = [&](int32_t st, const __bf16* qb, const __bf16* ob, int stage, const StepRsrc& rn, __bf16* qn,
+                       __bf16* on) {
       const int32_t rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
       // rows of this step that this wave's keys can see at all
-      if (rr >= w_hi || rr + kRowsPerStep <= w_lo) return;
+      if (rr >= w_hi || rr + kRowsPerStep <= w_lo) {
+        if constexpr (SPREAD) {
+#pragma unroll
+          for (int j = 0; j < QFULL; ++j) issue_seg(rn, qn, on, j);
+        }
+        return;
+      }
       // S = Q K^T and dP = dO V^T: C[row][key], lane = key, rows {8 a + 4 h + c}
       floatx16 s[NHALF], dp[NHALF];
 #pragma unroll
@@ -480,6 +514,17 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
           s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
           dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[hf], 0, 0, 0);
         }
+        constexpr int EVERY = (KS / QFULL >= 1) ? KS / QFULL : 1;
+        if (SPREAD && (ks % EVERY) == EVERY - 1 && ks / EVERY < QFULL) {
+          const int j = ks / EVERY;
+          const int seg = j * kBwdWaves + wv;
+          buffer_load_lds16(rn.q, qn + seg * 512, qoff[j]);
+          buffer_load_lds16(rn.o, on + seg * 512, qoff[j]);
+        }
+      }
+      if constexpr (SPREAD && KS / QFULL < 1) {
+#pragma unroll
+        for (int j = KS; j < QFULL; ++j) issue_seg(rn, qn, on, j);
       }
       bf16x8 pk[NHALF][2], dsk[NHALF][2];
 #pragma unroll
@@ -530,13 +575,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     };
 
     __syncthreads();  // the previous item no longer reads LDS (and s_rng is read)
-    if (nsteps > 0) issue(0, sQ0, sO0, 0);
+    if (nsteps > 0) issue(0, sQ0, sO0);
     auto step = [&](int32_t st, const __bf16* qc, const __bf16* oc, __bf16* qn, __bf16* on, int stage) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (tid < kRowsPerStep) { sL[stage][tid] = pend_l; sDl[stage][tid] = pend_d; }
       __syncthreads();
-      if (st + 1 < nsteps) issue(st + 1, qn, on, stage ^ 1);
-      compute(st, qc, oc, stage);
+      const StepRsrc rn = step_rsrc(st + 1);
+      if constexpr (!SPREAD) {
+#pragma unroll
+        for (int j = 0; j < QFULL; ++j) issue_seg(rn, qn, on, j);
+      }
+      issue_rest(rn, qn, on);
+      if (st + 1 < nsteps) issue_rows(st + 1);
+      compute(st, qc, oc, stage, rn, qn, on);
     };
     int32_t st = 0;
     for (; st + 1 < nsteps; st += 2) {
