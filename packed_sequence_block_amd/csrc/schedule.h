@@ -51,7 +51,8 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
                            int32_t nr, const ScheduleBuffers& buf, hipStream_t stream);
 
 // Document ids, run boundaries and the plan above for B rows at once, from boundaries
-// cu [B][n_docs + 1] (row stride cu_stride): two launches.
+// cu [B][n_docs + 1] (row stride cu_stride): one launch when B * ceil(L / 32) <= 2048,
+// else two.
 hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
                           int32_t seq_start, int32_t nr, int32_t* ids, int32_t* seg_cu, int32_t* seg_n,
                           const ScheduleBuffers& buf, int32_t* status, hipStream_t stream);

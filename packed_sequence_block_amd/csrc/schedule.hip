@@ -92,27 +92,32 @@ __device__ inline TileRecord make_record(const int32_t* __restrict__ blk_lo, con
   return r;
 }
 
-__global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t* __restrict__ blk_lo,
-                                                                  const int32_t* __restrict__ blk_hi,
-                                                                  int32_t B, int32_t nblk, int32_t nr,
-                                                                  int32_t ntile_row,
-                                                                  TileRecord* __restrict__ work) {
-  __shared__ int32_t hist[kBuckets];
-  __shared__ int32_t wsum[kSortThreads / kWave];
+// Records of all B * ntile_row row tiles into work[], longest key range first: a counting
+// sort over the tile count of each record's range (bucket kBuckets - 1 collects the
+// rest), done by one workgroup of NT threads.  hist: kBuckets ints of LDS, wsum: NT / 64.
+template <int NT>
+__device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_t B, int32_t nblk, int32_t nr,
+                            int32_t ntile_row, TileRecord* __restrict__ work, int32_t* hist, int32_t* wsum) {
+  static_assert(kBuckets % NT == 0, "buckets split evenly over the threads");
+  constexpr int PER = kBuckets / NT;  // consecutive buckets (in descending order) per thread
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int32_t T = B * ntile_row;
-  for (int i = tid; i < kBuckets; i += kSortThreads) hist[i] = 0;
+  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
   __syncthreads();
-  for (int32_t t = tid; t < T; t += kSortThreads) {
+  for (int32_t t = tid; t < T; t += NT) {
     const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
     atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
   }
   __syncthreads();
-  // exclusive scan in DESCENDING bucket order: offset(bk) = sum of hist[bk' > bk].
-  // Thread tid owns reversed buckets 2*tid and 2*tid+1.
-  const int r0 = 2 * tid, r1 = 2 * tid + 1;
-  const int32_t c0 = hist[kBuckets - 1 - r0], c1 = hist[kBuckets - 1 - r1];
-  int32_t inc = c0 + c1;
+  // exclusive scan in DESCENDING bucket order: offset(bk) = sum of hist[bk' > bk]
+  int32_t c[PER];
+  int32_t own = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    c[k] = hist[kBuckets - 1 - (PER * tid + k)];
+    own += c[k];
+  }
+  int32_t inc = own;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int32_t v = __shfl_up(inc, off, kWave);
@@ -120,18 +125,30 @@ __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t*
   }
   if (lane == kWave - 1) wsum[wv] = inc;
   __syncthreads();
-  int32_t base = 0;
-  for (int w = 0; w < wv; ++w) base += wsum[w];
-  const int32_t excl = base + inc - c0 - c1;
+  int32_t run = inc - own;
+  for (int w = 0; w < wv; ++w) run += wsum[w];
   __syncthreads();  // all reads of hist done before it is overwritten with offsets
-  hist[kBuckets - 1 - r0] = excl;
-  hist[kBuckets - 1 - r1] = excl + c0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    hist[kBuckets - 1 - (PER * tid + k)] = run;
+    run += c[k];
+  }
   __syncthreads();
-  for (int32_t t = tid; t < T; t += kSortThreads) {
+  for (int32_t t = tid; t < T; t += NT) {
     const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
     const int32_t bk = min(tile_iters(r.lo, r.hi), kBuckets - 1);
     work[atomicAdd(&hist[bk], 1)] = r;
   }
+}
+
+__global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t* __restrict__ blk_lo,
+                                                                  const int32_t* __restrict__ blk_hi,
+                                                                  int32_t B, int32_t nblk, int32_t nr,
+                                                                  int32_t ntile_row,
+                                                                  TileRecord* __restrict__ work) {
+  __shared__ int32_t hist[kBuckets];
+  __shared__ int32_t wsum[kSortThreads / kWave];
+  order_tiles<kSortThreads>(blk_lo, blk_hi, B, nblk, nr, ntile_row, work, hist, wsum);
 }
 
 // ---- key side (backward dK / dV) -----------------------------------------------------
@@ -199,17 +216,40 @@ __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restric
 //   * segments: one workgroup per row: the run boundaries of the ids the row will hold,
 //               from the boundaries (cu[0] when a non-empty document follows leading
 //               padding, and the end of every non-empty document short of S).
+//   * plan:     when B * nblk <= kPlanBlocks, one more workgroup computes every block's
+//               range itself (from the boundaries staged in LDS) and orders the row tiles
+//               as tile_order_kernel does, so the whole preparation is one launch.
 constexpr int kPrepThreads = 256;
+constexpr int kPlanBlocks = 2048;
+
+// key range [lo, hi) of 32-row query block blk from the row's boundaries cu[0..n_docs]
+__device__ inline void block_range_from_cu(const int32_t* cu, int32_t n_docs, int32_t blk, int32_t L,
+                                           int32_t seq_start, int32_t& lo, int32_t& hi) {
+  const int32_t c0 = cu[0], cn = cu[n_docs];
+  const int32_t r0 = seq_start + blk * kRowsPerBlock;
+  const int32_t r1 = seq_start + min(L, (blk + 1) * kRowsPerBlock);
+  const int32_t qf = max(r0, c0), ql = min(r1, cn) - 1;
+  lo = 0;
+  hi = 0;
+  if (qf <= ql) {
+    lo = cu[max(last_le(cu, n_docs + 1, qf), 0)];  // >= 0 for valid boundaries
+    hi = ql + 1;
+  }
+}
 
 __global__ void __launch_bounds__(kPrepThreads) prepare_kernel(
     const int32_t* __restrict__ cu_all, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
     int32_t seq_start, int32_t nblk, int32_t id_chunks, int32_t range_groups, int32_t* __restrict__ ids,
     int32_t* __restrict__ seg_cu, int32_t* __restrict__ seg_n, int32_t* __restrict__ blk_lo,
-    int32_t* __restrict__ blk_hi, int32_t* __restrict__ status) {
+    int32_t* __restrict__ blk_hi, int32_t* __restrict__ status, int32_t nr, int32_t ntile_row,
+    TileRecord* __restrict__ work, int32_t plan_in_grid) {
   constexpr int kCuStage = 4096;
   __shared__ int32_t scu[kCuStage];
   __shared__ int32_t wsum[kPrepThreads / kWave];
   __shared__ int32_t carry;
+  __shared__ int32_t hist[kBuckets];
+  __shared__ int32_t plo[kPlanBlocks];
+  __shared__ int32_t phi[kPlanBlocks];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int64_t id_blocks = (int64_t)B * id_chunks;
   const int64_t bx = blockIdx.x;
@@ -241,20 +281,29 @@ __global__ void __launch_bounds__(kPrepThreads) prepare_kernel(
     const int64_t w = (bx - id_blocks) * (kPrepThreads / kWave) + wv;
     if (w >= (int64_t)B * nblk) return;
     const int32_t b = (int32_t)(w / nblk), blk = (int32_t)(w % nblk);
-    const int32_t* cu = cu_all + (int64_t)b * cu_stride;
-    const int32_t c0 = cu[0], cn = cu[n_docs];
-    const int32_t r0 = seq_start + blk * kRowsPerBlock;
-    const int32_t r1 = seq_start + min(L, (blk + 1) * kRowsPerBlock);
-    const int32_t qf = max(r0, c0), ql = min(r1, cn) - 1;
-    int32_t lo = 0, hi = 0;
-    if (qf <= ql) {
-      lo = cu[max(last_le(cu, n_docs + 1, qf), 0)];  // >= 0 for valid boundaries
-      hi = ql + 1;
-    }
+    int32_t lo, hi;
+    block_range_from_cu(cu_all + (int64_t)b * cu_stride, n_docs, blk, L, seq_start, lo, hi);
     if (lane == 0) {
       blk_lo[w] = lo;
       blk_hi[w] = hi;
     }
+    return;
+  }
+  if (plan_in_grid && bx == id_blocks + range_groups + B) {
+    // the plan: block ranges into LDS (boundaries staged there when they fit), then the
+    // longest-first order of the row tiles
+    const int32_t ncu = n_docs + 1;
+    const bool staged = (int64_t)B * ncu <= kCuStage;  // uniform
+    if (staged)
+      for (int32_t j = tid; j < B * ncu; j += kPrepThreads) scu[j] = cu_all[(int64_t)(j / ncu) * cu_stride + j % ncu];
+    __syncthreads();
+    for (int32_t w = tid; w < B * nblk; w += kPrepThreads) {
+      const int32_t b = w / nblk;
+      const int32_t* cu = staged ? scu + b * ncu : cu_all + (int64_t)b * cu_stride;
+      block_range_from_cu(cu, n_docs, w % nblk, L, seq_start, plo[w], phi[w]);
+    }
+    __syncthreads();
+    order_tiles<kPrepThreads>(plo, phi, B, nblk, nr, ntile_row, work, hist, wsum);
     return;
   }
   // segments of row b
@@ -408,13 +457,16 @@ hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, 
   const int32_t id_chunks = (S + kPrepThreads - 1) / kPrepThreads;
   const int64_t waves_per_wg = kPrepThreads / kWave;
   const int32_t range_groups = (int32_t)(((int64_t)B * nblk + waves_per_wg - 1) / waves_per_wg);
-  const int64_t grid = (int64_t)B * id_chunks + range_groups + B;
+  const int32_t ntile_row = (nblk + nr - 1) / nr;
+  // small plans are ordered by one extra workgroup of the same grid; larger ones by
+  // tile_order_kernel afterwards
+  const bool fused = nblk > 0 && (int64_t)B * nblk <= kPlanBlocks;
+  const int64_t grid = (int64_t)B * id_chunks + range_groups + B + (fused ? 1 : 0);
   prepare_kernel<<<dim3((unsigned)grid), dim3(kPrepThreads), 0, stream>>>(
       cu, cu_stride, n_docs, B, S, L, seq_start, nblk, id_chunks, range_groups, ids, seg_cu, seg_n, buf.blk_lo,
-      buf.blk_hi, status);
+      buf.blk_hi, status, nr, ntile_row, buf.work, fused ? 1 : 0);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nblk == 0) return e;
-  const int32_t ntile_row = (nblk + nr - 1) / nr;
+  if (e != hipSuccess || nblk == 0 || fused) return e;
   tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
                                                                 buf.work);
   return hipGetLastError();
