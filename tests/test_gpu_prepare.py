@@ -113,3 +113,23 @@ def test_attention_on_prepared_plan(psb):
     ref = psb.blockdiag_attn_fwd(q, k, v, ids, lay.seq_start, None, lay.enable_gqa)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_plan_sizes_around_the_single_launch_limit(psb):
+    # one launch orders the plan while B * ceil(L / 32) <= 2048; past that a second kernel
+    # does; both must give a valid plan and the same attention
+    rng = np.random.default_rng(1601)
+    for B, S in ((1, 65536), (1, 65537), (3, 22000)):
+        rows = [random_cu(rng, S) for _ in range(B)]
+        say("prepare limit", "B", B, "S", S, "blocks", B * ((S + 31) // 32))
+        check(psb, rows, S, S, 0, 8, 2, 128)
+
+
+def test_plan_with_boundaries_too_many_to_stage(psb):
+    # B * (documents + 1) above the 4096 boundaries the plan workgroup stages in LDS: it reads
+    # them from memory instead
+    B, S = 3, 6000
+    rows = [np.arange(0, S + 1, 1 + b, dtype=np.int32) for b in range(B)]
+    say("prepare many documents", [len(r) - 1 for r in rows])
+    check(psb, rows, S, S, 0, 4, 4, 64)
+    check(psb, rows, S, 1000, 2500, 4, 4, 64)
