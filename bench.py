@@ -104,7 +104,7 @@ def backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
     torch.cuda.synchronize()
     ms = timed(bwd, max(5, steps // 2))
     flops = 2.5 * lay.useful_flops()
-    return {"what": "dq, dk, dv from dout (delta, dq and dk/dv kernels)", "ms": round(ms, 5),
+    return {"what": "dq, dk, dv from dout (dq with delta, then dk/dv kernels)", "ms": round(ms, 5),
             "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
             "pct_of_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
             "flop_convention": "2.5 x forward useful flops"}

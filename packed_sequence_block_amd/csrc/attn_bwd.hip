@@ -10,12 +10,13 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over a kv
 //   head's query heads)
 //
-// Three kernels:
-//   delta_kernel  rowsum(dO * O) in fp32, one 16-lane group per row;
+// Two kernels:
 //   dq_kernel     query-stationary like the forward: a wave owns 32 query rows of one
-//                 head, walks the key tiles of the forward's plan, recomputes S^T and
-//                 dP^T = V dO^T (lane = row), and accumulates dQ^T += K^T dS^T with
-//                 the K^T operand gathered from the K tile by transposing LDS reads;
+//                 head, computes their delta = rowsum(dO * O) in fp32 from the rows it
+//                 loads anyway (and stores it for dkdv_kernel), walks the key tiles of the
+//                 forward's plan, recomputes S^T and dP^T = V dO^T (lane = row), and
+//                 accumulates dQ^T += K^T dS^T with the K^T operand gathered from the K
+//                 tile by transposing LDS reads;
 //   dkdv_kernel   key-stationary: a wave owns 32 keys of one kv head (K and V held in
 //                 VGPRs as MFMA B operands), a workgroup 128 keys; it walks every query
 //                 head of the group and the 32-row query tiles that can see its keys,
@@ -49,8 +50,9 @@ struct BwdParams {
   const __bf16* k;     // [B, Hkv, kv_len, D]: keys at global positions [kv_start, kv_start + kv_len)
   const __bf16* v;
   const __bf16* dout;  // [B, Hq, L, D]
+  const __bf16* out;   // [B, Hq, L, D]: the forward's output
   const float* lse;    // [B, Hq, L] natural log
-  const float* delta;  // [B, Hq, L]
+  float* delta;        // [B, Hq, L]: written by dq_kernel, read by dkdv_kernel
   const int32_t* doc;  // [B, S]
   __bf16* dq;          // [B, Hq, L, D]
   __bf16* dk;          // [B, Hkv, kv_len, D]
@@ -66,26 +68,6 @@ struct BwdParams {
   int32_t kv_start, kv_len;
   int32_t* status;          // PSB_DATA_KV_WINDOW when a row needs a key before kv_start, or null
 };
-
-// ---- delta = rowsum(dO * O) --------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) delta_kernel(const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
-                                                    float* __restrict__ delta, int64_t rows) {
-  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int part = (int)(gid % LPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 o = *(const bf16x8*)(out + row * D + 8 * part);
-    const bf16x8 g = *(const bf16x8*)(dout + row * D + 8 * part);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc += (float)o[t] * (float)g[t];
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-  if (row < rows && part == 0) delta[row] = acc;
-}
 
 // ---- dQ: query-stationary ---------------------------------------------------------
 template <int D, int NH>
@@ -142,6 +124,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     __bf16* dq_row = p.dq + qrow * D;
     if (thi <= tlo) {
       if (row_in) {
+        // no key for any row of the tile: P is 0 for all of them, any finite delta will do
+        if (h == 0) p.delta[qrow] = 0.f;
         const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -203,7 +187,23 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     }
     // exp2 argument offset of the row (rows without keys never produce a P: any finite value)
     const float lse2 = (valid && row_in) ? p.lse[qrow] * kLog2e : 0.f;
-    const float dlt = row_in ? p.delta[qrow] : 0.f;
+    // delta = rowsum(dO * O): this lane's 64 (D = 128) or 32 d of the row, then the partner
+    // lane's half (lane ^ 32 holds the other d)
+    float dlt;
+    {
+      float part = 0.f;
+      if (row_in) {
+        const __bf16* osrc2 = p.out + qrow * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 o8 = *(const bf16x8*)(osrc2 + 16 * ks + 8 * h);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) part = __builtin_fmaf((float)o8[t], (float)oreg[ks][t], part);
+        }
+      }
+      dlt = partner_sum(part);
+      if (row_in && h == 0) p.delta[qrow] = dlt;
+    }
 
     floatx16 acc[DB];
 #pragma unroll
@@ -631,13 +631,9 @@ int64_t bwd_plan_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L) {
 int64_t bwd_delta_bytes(int64_t B, int64_t Hq, int64_t L) { return pad256(4 * B * Hq * L); }
 
 template <int D>
-hipError_t launch_bwd(int nh, const BwdParams& prm, const __bf16* out, float* delta, int64_t rows, hipStream_t s) {
+hipError_t launch_bwd(int nh, const BwdParams& prm, int64_t rows, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (rows > 0) {  // L == 0: no query rows, dq is empty and dk / dv are all zero
-    const int64_t threads = rows * (D / 8);
-    delta_kernel<D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(out, prm.dout, delta, rows);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const unsigned qgrid = (unsigned)prm.items;
     switch (nh) {
       case 4: dq_kernel<D, 4><<<dim3(qgrid), dim3(kBwdThreads), 0, s>>>(prm); break;
@@ -716,6 +712,7 @@ psb_status bwd_run(const void* q, const void* k, const void* v, const void* out,
   prm.dout = static_cast<const __bf16*>(dout);
   prm.lse = lse;
   prm.delta = delta;
+  prm.out = static_cast<const __bf16*>(out);
   prm.doc = doc_ids;
   prm.dq = static_cast<__bf16*>(dq);
   prm.dk = static_cast<__bf16*>(dk);
@@ -739,8 +736,8 @@ psb_status bwd_run(const void* q, const void* k, const void* v, const void* out,
                           (int32_t)kv_len, klo, khi, kwork, as_stream(stream)) != hipSuccess)
     return PSB_ERR_HIP;
   const hipError_t e = (D == 128)
-      ? launch_bwd<128>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream))
-      : launch_bwd<64>((int)nh, prm, static_cast<const __bf16*>(out), delta, rows, as_stream(stream));
+      ? launch_bwd<128>((int)nh, prm, rows, as_stream(stream))
+      : launch_bwd<64>((int)nh, prm, rows, as_stream(stream));
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }
 
