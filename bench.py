@@ -5,7 +5,8 @@
 One step = the whole device path over one batch of synthetic packed rows that
 is already resident in HBM:
   step preparation for all rows (document ids, run boundaries, tile plan: one
-  kernel plus the plan's sort) -> block-diagonal attention kernel.
+  kernel, one of whose workgroups orders the row tiles) -> block-diagonal
+  attention kernel.
 The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
 
 Default workload: the packed LLM row (B=1, S=L=8192, Hq=32, Hkv=8, D=128,
@@ -310,7 +311,7 @@ def main():
     cup, segp, segnp = P(cu_all), P(seg_cu), P(seg_n)
 
     def prepare():
-        # the step's ids, run boundaries and plan for all rows: two launches
+        # the step's ids, run boundaries and plan for all rows: one launch
         st = lib.psb_blockdiag_prepare(cup, n1, n1 - 1, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, dp, segp, segnp,
                                        wp, ws_bytes, None, sptr)
         assert st == 0, st

@@ -234,8 +234,9 @@ psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, const vo
                                           size_t workspace_bytes, int32_t* status_word, void* stream);
 
 /*
- * The whole preparation of a step in two launches: document ids, run boundaries and the
- * attention plan for B rows at once from their boundaries (glm5_next.cp page,
+ * The whole preparation of a step in one launch (two when B * ceil(L / 32) > 2048):
+ * document ids, run boundaries and the attention plan for B rows at once from their
+ * boundaries (glm5_next.cp page,
  * doc_ids_from_cu_seqlens and segment_cu_seqlens; blockdiag_cp package overview,
  * "varlen metadata precompute").  Outputs equal those of psb_doc_ids_from_cu_seqlens and
  * psb_segment_cu_seqlens run on each row, and of psb_blockdiag_attn_plan on the ids.

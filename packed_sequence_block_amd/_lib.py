@@ -545,7 +545,7 @@ def masked_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: tor
 def blockdiag_prepare(cu_seqlens: torch.Tensor, seq_len: int, Hq: int, Hkv: int, D: int, seq_start: int = 0,
                       L: int | None = None, enable_gqa: bool = False, workspace: torch.Tensor | None = None,
                       validate: bool = False):
-    """One step's preparation for B rows in two launches, from boundaries ``[B, N + 1]``
+    """One step's preparation for B rows in one launch, from boundaries ``[B, N + 1]``
     (rows with fewer documents repeat their last boundary): returns ``(doc_ids [B, S],
     seg_cu [B, S + 1], seg_n [B], workspace)``; row b's run boundaries are
     ``seg_cu[b, :seg_n[b] + 1]`` and the workspace holds the attention plan for
