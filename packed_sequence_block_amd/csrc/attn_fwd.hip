@@ -219,8 +219,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       }
     };
     // ---- this item's Q^T operand, document id and block start ---------------------------
-    // All loads that depend only on the record are issued before the tile-0 loads, so that
-    // waiting for them (vmcnt counts in issue order) does not wait for tile 0 as well.
+    // The loads that depend only on the record go out first, then the tile-0 loads, so all of
+    // them are in flight together (the first use of the document id still waits for most of
+    // tile 0: vmcnt counts in issue order).
     bf16x8 qreg[KS];
     {
       const __bf16* qsrc = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)row_local * p.q_ss;
