@@ -277,17 +277,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     if (t < ntiles) step(t, sK0, sK1, sV0, sV1);
 
     // ---- epilogue: dQ = scale * dQ^T, bf16 ------------------------------------------------
-    if (row_in) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 w;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) w[u] = (__bf16)(acc[db][4 * g4 + u] * p.scale);
-          *(bf16x4*)(dq_row + 32 * db + 8 * g4 + 4 * h) = w;
-        }
-    }
+    for (int db = 0; db < DB; ++db) store_block_bf16(dq_row + 32 * db, acc[db], p.scale, row_in, h);
   }
 }
 
@@ -596,24 +587,16 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     }
     if (st < nsteps) step(st, sQ0, sO0, sQ1, sO1, 0);
 
-    // ---- epilogue: C[d][key] -> dk, dv rows (lane = key, 4 consecutive d per store) -------
-    if (key_in) {
+    // ---- epilogue: C[d][key] -> dk, dv rows (lane = key) ------------------------------------
+    {
       const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
       __bf16* dkr = p.dk + kvrow * D;
       __bf16* dvr = p.dv + kvrow * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 wk, wvv;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            wk[u] = (__bf16)(dka[db][4 * g4 + u] * p.scale);
-            wvv[u] = (__bf16)dva[db][4 * g4 + u];
-          }
-          *(bf16x4*)(dkr + 32 * db + 8 * g4 + 4 * h) = wk;
-          *(bf16x4*)(dvr + 32 * db + 8 * g4 + 4 * h) = wvv;
-        }
+      for (int db = 0; db < DB; ++db) {
+        store_block_bf16(dkr + 32 * db, dka[db], p.scale, key_in, h);
+        store_block_bf16(dvr + 32 * db, dva[db], 1.f, key_in, h);
+      }
     }
   }
 }

@@ -14,6 +14,7 @@ typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -47,6 +48,36 @@ __device__ __forceinline__ float partner_max(float x) {
 __device__ __forceinline__ float partner_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Stores one 32 x 32 fp32 MFMA block as bf16 into this lane's output row: the lane
+// (row = lane & 31, h = lane >> 5) holds d = 8 g4 + 4 h + {0..3} (g4 = 0..3) at acc[4 g4 ..].
+// One swap with the partner lane (lane ^ 32, same row) per pair of g4 leaves lane h with
+// d = 16 pr + 8 h + {0..7} (pr = 0, 1), so each of the two stores writes 16 bytes per lane and
+// 32 contiguous bytes per row.  Every lane must call it (the swap is cross-lane); only lanes
+// with `in` store.  row points at the block's first element of this lane's row; h = lane >> 5.
+__device__ __forceinline__ void store_block_bf16(__bf16* row, const floatx16& acc, float mul, bool in, int h) {
+  uint32_t w[4][2];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    w[g4][0] = __builtin_bit_cast(uint32_t, cvt_bf16x2(acc[4 * g4] * mul, acc[4 * g4 + 1] * mul));
+    w[g4][1] = __builtin_bit_cast(uint32_t, cvt_bf16x2(acc[4 * g4 + 2] * mul, acc[4 * g4 + 3] * mul));
+  }
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int dw = 0; dw < 2; ++dw) {
+      const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][dw], w[2 * pr + 1][dw], false, false);
+      w[2 * pr][dw] = r[0];
+      w[2 * pr + 1][dw] = r[1];
+    }
+  if (in) {
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const u32x4v v4 = {w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
+      *(u32x4v*)(row + 16 * pr + 8 * h) = v4;
+    }
+  }
 }
 
 }  // namespace

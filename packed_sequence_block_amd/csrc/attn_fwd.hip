@@ -486,35 +486,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       const float lse2 = (l_tot > 0.f) ? m_run * sc + __log2f(l_tot) : -INFINITY;
       p.lse[((int64_t)b * p.Hq + hq) * p.L + row_local] = lse2 * 0.69314718055994531f;
     }
-    // A lane holds d = 32 db + 8 g4 + 4 h + {0..3} of its row; one swap with the partner lane
-    // (lane ^ 32, same row) per pair of g4 leaves lane h with d 32 db + 8 (g4 pair) + 8 h +
-    // {0..7}, so every store writes 16 bytes per lane and 32 contiguous bytes per row.
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      uint32_t w[4][2];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const bf16x2 lo2 = cvt_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv);
-        const bf16x2 hi2 = cvt_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-        w[g4][0] = __builtin_bit_cast(uint32_t, lo2);
-        w[g4][1] = __builtin_bit_cast(uint32_t, hi2);
-      }
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-        for (int dw = 0; dw < 2; ++dw) {
-          const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][dw], w[2 * pr + 1][dw], false, false);
-          w[2 * pr][dw] = r[0];
-          w[2 * pr + 1][dw] = r[1];
-        }
-      if (row_in) {
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          u32x4 v4 = {w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
-          *(u32x4*)(out_row + 32 * db + 16 * pr + 8 * h) = v4;
-        }
-      }
-    }
+    for (int db = 0; db < DB; ++db) store_block_bf16(out_row + 32 * db, o[db], inv, row_in, h);
   }  // item loop
 }
 
