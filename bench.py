@@ -1,6 +1,7 @@
 """Benchmark of the packed block-causal attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--sub-configs 2,3,4]
+                    [--no-cpu-baseline] [--no-backward] [--no-dense]
 
 One step = the whole device path over one batch of synthetic packed rows that
 is already resident in HBM:
@@ -9,18 +10,19 @@ is already resident in HBM:
   attention kernel.
 The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
 
-Default workload: the packed LLM row (B=1, S=L=8192, Hq=32, Hkv=8, D=128,
-uniform[128, 2048] document lengths, 107-token padding tail, seed 2).
-Prints ONE JSON line.  The timed steps carry no events (an event record between
-two launches costs the queue a few microseconds).  `roofline` describes the
-attention kernel alone, timed with HIP events on the stream it is launched on
-around K back-to-back launches after the timed steps; `phase_ms` times the
-preparation the same way, and for reference the separate per-row boundary calls
-and plan call that compute the same outputs.  `traffic` is HBM bytes per launch
-from the committed rocprofv3 counter runs, reported only while the kernel
-source is unchanged; `backward` times the training path's backward (dq, dk, dv)
-on the same workload; `cpu_baseline` times the CPU fp64 oracle on the host cores
-over the same workload.
+Headline workload (default --config 5): the long mixed row (B=1, S=L=65536,
+Hq=64, Hkv=4, D=64, 80% uniform[64, 1024] / 20% uniform[8192, 24576] document
+lengths, seed 5), the largest of the five workloads.  Exactly K steps are timed
+by the wall clock between two device synchronizations; inside that window an
+event pair on the launch stream brackets every attention launch, so
+`roofline.kernel_ms` (the mean of those launch durations) is measured over the
+same steps and never exceeds `ms_per_step`.  `sub_configs` repeats the same
+measurement for workloads 2-4 (five repeats of enough steps to last >= 100 ms,
+median reported).  `traffic` is HBM bytes per launch from the committed
+rocprofv3 counter runs, reported only while the kernel source is unchanged;
+`backward` times the training path's backward (dq, dk, dv); `cpu_baseline`
+times the CPU fp64 oracle on the host cores over a bounded sample of the
+headline workload.
 """
 
 from __future__ import annotations
@@ -30,6 +32,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -48,35 +51,53 @@ def attn_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    or None when they were taken on another kernel source or workload."""
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, or None
+    when they were taken on another kernel source or do not cover the workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != attn_source_hash() or rec.get("workload") != workload:
+    if rec.get("source_sha256_16") != attn_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(lay, q, k, v, budget_s: float = 10.0, max_passes: int = 40):
+def cpu_baseline(lay, q, k, v, budget_s: float = 15.0, max_passes: int = 40):
+    """The oracle as it stands (torch-CPU fp64, chunked explicit mask) on the host cores.
+    A bounded sample: the whole workload when one pass is cheap, else the first query
+    heads of kv head 0 (a subset of the same attention problem), scaled to TFLOP/s on
+    the useful flops of exactly that sample."""
+    import numpy as np
     import torch
     import oracle
-    ids = [oracle.doc_ids_from_cu_seqlens(lay.cu_seqlens(b), lay.S)[0] for b in range(lay.B)]
-    import numpy as np
-    ids = np.stack(ids)
+    aff = len(os.sched_getaffinity(0))
+    threads = max(1, min(aff, torch.get_num_threads()))
+    torch.set_num_threads(threads)
+    ids = np.stack([oracle.doc_ids_from_cu_seqlens(lay.cu_seqlens(b), lay.S)[0] for b in range(lay.B)])
+    heads = lay.Hq
+    if lay.useful_flops() > 1e12:   # one whole pass would take well over a minute
+        heads = min(lay.Hq // lay.Hkv, 8)
+    qs, ks, vs = q[:, :heads], k[:, :max(1, heads * lay.Hkv // lay.Hq)], v[:, :max(1, heads * lay.Hkv // lay.Hq)]
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.blockdiag_attn(q, k, v, ids, lay.seq_start, None, lay.enable_gqa)
+        oracle.blockdiag_attn(qs, ks, vs, ids, lay.seq_start, None, lay.enable_gqa)
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= max_passes:
             break
-    flops = lay.useful_flops() * passes
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
-            "kind": "oracle",
-            "sample": f"whole workload x{passes} (all {lay.B} rows, {lay.Hq} heads), {el:.1f} s, fp64 torch-CPU"}
+    flops = lay.useful_flops() * heads / lay.Hq * passes
+    cfg = torch.__config__.show()
+    blas = next((t.split("=")[1] for t in cfg.replace(",", " ").split() if t.startswith("BLAS_INFO=")), "unknown")
+    par = next((ln.split(":", 1)[1].strip() for ln in torch.__config__.parallel_info().splitlines()
+                if ln.startswith("ATen parallel backend")), "unknown")
+    what = (f"whole workload x{passes} (all {lay.B} rows, {lay.Hq} heads)" if heads == lay.Hq else
+            f"query heads 0-{heads - 1} (kv head 0) of all {lay.B} row(s), x{passes}")
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {el:.1f} s, fp64 torch-CPU",
+            "threads_note": f"torch threads {threads} of {aff} CPUs in the affinity mask",
+            "blas": blas, "parallel_backend": par}
 
 
 def backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, steps, timed):
@@ -252,15 +273,141 @@ def dropin_leg(psb, lay, q, k, v, doc_ids, steps):
     return res
 
 
+class Problem:
+    """One workload resident on the device, with the step's two launches as closures."""
+
+    def __init__(self, psb, lib, c, dev):
+        import torch
+        from workloads import make_layout, make_qkv
+        self.lay = lay = make_layout(c)
+        self.q_cpu, self.k_cpu, self.v_cpu = make_qkv(lay)
+        self.q, self.k, self.v = self.q_cpu.to(dev), self.k_cpu.to(dev), self.v_cpu.to(dev)
+        B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
+        cus = [torch.as_tensor(lay.cu_seqlens(b)).to(dev) for b in range(B)]
+        self.doc_ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+        self.seg_cu = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
+        self.seg_n = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.ws_bytes = ws_bytes = psb.workspace_size(B, Hq, Hkv, L, D)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        sptr = ctypes.c_void_p(self.stream.cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        scale = float(D) ** -0.5
+        gqa = 1 if lay.enable_gqa else 0
+        row_ptrs = [(P(cus[b]), cus[b].numel() - 1, ctypes.c_void_p(self.doc_ids[b].data_ptr()),
+                     ctypes.c_void_p(self.seg_cu[b].data_ptr()), ctypes.c_void_p(self.seg_n[b:].data_ptr()))
+                    for b in range(B)]
+        qp, kp, vp, dp, op, wp = P(self.q), P(self.k), P(self.v), P(self.doc_ids), P(self.out), P(self.ws)
+        # all rows' boundaries as one [B, N + 1] table (shorter rows repeat their last boundary)
+        n1 = max(c_.numel() for c_ in cus)
+        self.cu_all = torch.stack([torch.cat([c_, c_[-1:].expand(n1 - c_.numel())]) for c_ in cus]).to(
+            torch.int32).contiguous()
+        cup, segp, segnp = P(self.cu_all), P(self.seg_cu), P(self.seg_n)
+
+        def prepare():
+            # the step's ids, run boundaries and plan for all rows: one launch
+            st = lib.psb_blockdiag_prepare(cup, n1, n1 - 1, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, dp, segp,
+                                           segnp, wp, ws_bytes, None, sptr)
+            assert st == 0, st
+
+        def boundary():
+            for cu_p, nd, ids_p, scu_p, sn_p in row_ptrs:
+                st = lib.psb_doc_ids_from_cu_seqlens(cu_p, nd, S, ids_p, None, sptr)
+                assert st == 0, st
+                st = lib.psb_segment_cu_seqlens(ids_p, S, scu_p, S + 1, sn_p, sptr)
+                assert st == 0, st
+
+        def plan():
+            st = lib.psb_blockdiag_attn_plan(dp, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, wp, ws_bytes, sptr)
+            assert st == 0, st
+
+        def attention():
+            st = lib.psb_blockdiag_attn_fwd_planned(qp, kp, vp, dp, B, Hq, Hkv, L, S, D, None, None,
+                                                    lay.seq_start, scale, gqa, op, wp, ws_bytes, None, sptr)
+            assert st == 0, st
+
+        self.prepare, self.boundary, self.plan, self.attention = prepare, boundary, plan, attention
+
+    def timed(self, fn, n):
+        """n back-to-back calls between one pair of events on the launch stream (ms per call)."""
+        import torch
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(self.stream)
+        for _ in range(n):
+            fn()
+        a1.record(self.stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / n
+
+    def time_steps(self, n):
+        """n steps between two device synchronizations, wall clock; an event pair on the
+        launch stream around each attention launch.  Returns (ms per step, mean ms per
+        attention launch, [ms per launch])."""
+        import torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in evs:
+            self.prepare()
+            a.record(self.stream)
+            self.attention()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        kern = [a.elapsed_time(b) for a, b in evs]
+        return ms, sum(kern) / n, kern
+
+
+def _rates(lay, ms_step, kernel_ms):
+    flops = lay.useful_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    return value, achieved
+
+
+def sub_record(psb, lib, c, dev, args, legs):
+    """Workload c measured like the headline: repeats of enough steps to last >= 100 ms,
+    median of the repeats."""
+    import torch
+    pb = Problem(psb, lib, c, dev)
+    lay = pb.lay
+    for _ in range(3):
+        pb.prepare()
+        pb.attention()
+    est, _, _ = pb.time_steps(3)
+    n = max(5, int(100.0 / max(est, 1e-3)) + 1)
+    reps = [pb.time_steps(n) for _ in range(5)]
+    ms_step = statistics.median(r[0] for r in reps)
+    kernel_ms = statistics.median(r[1] for r in reps)
+    assert kernel_ms <= ms_step * 1.001, (c, kernel_ms, ms_step)
+    value, achieved = _rates(lay, ms_step, kernel_ms)
+    rec = {"workload": lay.name, "value": round(value, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_step, 5),
+           "steps_per_repeat": n, "repeats": 5, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+           "allowed_pairs": lay.allowed_pairs(), "useful_gflop_per_step": round(lay.useful_flops() / 1e9, 3),
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic(lay.name), "kernel": "attn_fwd_kernel",
+                        "kernel_ms": round(kernel_ms, 5)}}
+    for name, fn in legs:
+        rec[name] = fn(pb)
+    del pb
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--sub-configs", default="2,3,4", help="comma-separated workloads also measured ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the training-path (backward) timing")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-mask path timing")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="time the step alone: no legs, no sub-configs, no CPU baseline (for profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -280,110 +427,68 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n}))
         return
     import packed_sequence_block_amd as psb
-    from workloads import make_layout, make_qkv
 
     lib = psb.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lay = make_layout(args.config)
-    q_cpu, k_cpu, v_cpu = make_qkv(lay)
-    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    pb = Problem(psb, lib, args.config, dev)
+    lay = pb.lay
     B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
-    cus = [torch.as_tensor(lay.cu_seqlens(b)).to(dev) for b in range(B)]
-    doc_ids = torch.empty((B, S), dtype=torch.int32, device=dev)
-    seg_cu = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
-    seg_n = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws_bytes = psb.workspace_size(B, Hq, Hkv, L, D)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    scale = float(D) ** -0.5
-    gqa = 1 if lay.enable_gqa else 0
-    row_ptrs = [(P(cus[b]), cus[b].numel() - 1, ctypes.c_void_p(doc_ids[b].data_ptr()),
-                 ctypes.c_void_p(seg_cu[b].data_ptr()), ctypes.c_void_p(seg_n[b:].data_ptr()))
-                for b in range(B)]
-    qp, kp, vp, dp, op, wp = P(q), P(k), P(v), P(doc_ids), P(out), P(ws)
-    # all rows' boundaries as one [B, N + 1] table (shorter rows repeat their last boundary)
-    n1 = max(c.numel() for c in cus)
-    cu_all = torch.stack([torch.cat([c, c[-1:].expand(n1 - c.numel())]) for c in cus]).to(torch.int32).contiguous()
-    cup, segp, segnp = P(cu_all), P(seg_cu), P(seg_n)
-
-    def prepare():
-        # the step's ids, run boundaries and plan for all rows: one launch
-        st = lib.psb_blockdiag_prepare(cup, n1, n1 - 1, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, dp, segp, segnp,
-                                       wp, ws_bytes, None, sptr)
-        assert st == 0, st
-
-    def boundary():
-        for cu_p, nd, ids_p, scu_p, sn_p in row_ptrs:
-            st = lib.psb_doc_ids_from_cu_seqlens(cu_p, nd, S, ids_p, None, sptr)
-            assert st == 0, st
-            st = lib.psb_segment_cu_seqlens(ids_p, S, scu_p, S + 1, sn_p, sptr)
-            assert st == 0, st
-
-    def plan():
-        st = lib.psb_blockdiag_attn_plan(dp, B, Hq, Hkv, L, S, D, lay.seq_start, gqa, wp, ws_bytes, sptr)
-        assert st == 0, st
-
-    def attention():
-        st = lib.psb_blockdiag_attn_fwd_planned(qp, kp, vp, dp, B, Hq, Hkv, L, S, D, None, None, lay.seq_start,
-                                                scale, gqa, op, wp, ws_bytes, None, sptr)
-        assert st == 0, st
-
-    def step():
-        prepare()
-        attention()
 
     for _ in range(args.warmup):
-        step()
+        pb.prepare()
+        pb.attention()
     torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize(dev)
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-
-    def timed(fn, n):
-        # n back-to-back calls between one pair of events on the launch stream
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        for _ in range(n):
-            fn()
-        a1.record(stream)
-        torch.cuda.synchronize(dev)
-        return a0.elapsed_time(a1) / n
-
-    attn_ms = timed(attention, args.steps)
-    phase_ms = {"prepare": round(timed(prepare, args.steps), 5), "attention": round(attn_ms, 5),
-                "separate_calls": {"boundary_per_row": round(timed(boundary, args.steps), 5),
-                                   "plan": round(timed(plan, args.steps), 5)}}
-    flops = lay.useful_flops()
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(lay.name)
+    ms_step, kernel_ms, per_launch = pb.time_steps(args.steps)
+    assert kernel_ms <= ms_step, f"attention launches ({kernel_ms} ms) longer than the step ({ms_step} ms)"
+    value, achieved = _rates(lay, ms_step, kernel_ms)
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": lay.name, "B": B, "S": S, "L": L, "seq_start": lay.seq_start, "Hq": Hq,
                    "Hkv": Hkv, "D": D, "documents": sum(len(r) for r in lay.doc_lens),
-                   "allowed_pairs": lay.allowed_pairs(), "useful_gflop_per_step": round(flops / 1e9, 3),
+                   "allowed_pairs": lay.allowed_pairs(), "useful_gflop_per_step": round(lay.useful_flops() / 1e9, 3),
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 5)},
-        "phase_ms": phase_ms,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(lay.name),
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_min": round(min(per_launch), 5), "kernel_ms_max": round(max(per_launch), 5),
+                     "timing": "mean of per-launch event pairs inside the timed steps"},
     }
-    if not args.no_dense:
-        rec["dense_mask"] = dense_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
-    rec["boundary_variants"] = variants_leg(psb, lay, stream, args.steps, timed)
-    rec["drop_in"] = dropin_leg(psb, lay, q, k, v, doc_ids, args.steps)
-    rec["kv_window"] = window_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
+    if args.only_attention:
+        print(json.dumps(rec), flush=True)
+        return
+    rec["phase_ms"] = {"prepare": round(pb.timed(pb.prepare, args.steps), 5),
+                       "separate_calls": {"boundary_per_row": round(pb.timed(pb.boundary, args.steps), 5),
+                                          "plan": round(pb.timed(pb.plan, args.steps), 5)}}
+    rec["boundary_variants"] = variants_leg(psb, lay, pb.stream, args.steps, pb.timed)
     if not args.no_backward:
-        rec["backward"] = backward_leg(psb, lib, lay, q, k, v, doc_ids, stream, args.steps, timed)
+        rec["backward"] = backward_leg(psb, lib, lay, pb.q, pb.k, pb.v, pb.doc_ids, pb.stream, args.steps, pb.timed)
+    q_cpu, k_cpu, v_cpu = pb.q_cpu, pb.k_cpu, pb.v_cpu
+    del pb
+    torch.cuda.empty_cache()
+
+    subs = {}
+    for c in [int(x) for x in args.sub_configs.split(",") if x.strip()]:
+        if c == args.config:
+            continue
+        legs = []
+        if not args.no_backward:
+            legs.append(("backward", lambda p: backward_leg(psb, lib, p.lay, p.q, p.k, p.v, p.doc_ids, p.stream,
+                                                            20, p.timed)))
+        if c == 2:
+            if not args.no_dense:
+                legs.append(("dense_mask", lambda p: dense_leg(psb, lib, p.lay, p.q, p.k, p.v, p.doc_ids, p.stream,
+                                                               20, p.timed)))
+            legs.append(("drop_in", lambda p: dropin_leg(psb, p.lay, p.q, p.k, p.v, p.doc_ids, 20)))
+        if c == 3:
+            legs.append(("kv_window", lambda p: window_leg(psb, lib, p.lay, p.q, p.k, p.v, p.doc_ids, p.stream, 20,
+                                                           p.timed)))
+        subs[str(c)] = sub_record(psb, lib, c, dev, args, legs)
+        print(f"[bench] workload {c} done", file=sys.stderr, flush=True)
+    if subs:
+        rec["sub_configs"] = subs
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lay, q_cpu, k_cpu, v_cpu)
     print(json.dumps(rec), flush=True)

@@ -185,14 +185,19 @@ size_t psb_blockdiag_attn_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv,
  *   q_strides    host int64[3] = strides of (B, H, seq) in elements, or NULL for
  *                contiguous [B, Hq, L, D]; kv_strides likewise for k and v.
  *   seq_start    global position of local row 0; 0 <= seq_start, seq_start + L <= S.
- *   scale        softmax scale (finite, > 0 not required); callers pass D**-0.5 for
- *                the default.
+ *   scale        softmax scale (finite, any sign; callers pass D**-0.5 for the default).
+ *                0 and -0 weigh every allowed key equally (each row is the mean of v
+ *                over its document prefix).
  *   enable_gqa   non-zero: query head h reads kv head h / (Hq / Hkv) (Hq % Hkv == 0).
  *                Zero: requires Hq == Hkv, else PSB_ERR_SHAPE.
  *   out          device bf16 [B, Hq, L, D], contiguous; must not alias q, k or v.
  *   workspace    device, >= psb_blockdiag_attn_fwd_workspace_size(...) bytes,
  *                16-byte aligned (scheduler tables; contents need no initialisation).
- *   status_word  device int32 or NULL (unused by this call at present).
+ *   status_word  device int32 or NULL.  When non-NULL the call also enqueues the check of
+ *                the doc_ids precondition (one extra launch after the attention kernel)
+ *                and ORs PSB_DATA_DOC_NOT_CONTIGUOUS into the word when a non-padding id
+ *                occurs in two separate runs of a row; the output is then unspecified.
+ *                NULL skips the check.
  *
  * D must be 64 or 128 (else PSB_ERR_UNSUPPORTED).  Empty problems (B, Hq, L == 0)
  * enqueue nothing and return PSB_OK.
@@ -302,7 +307,11 @@ psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, cons
  *                of this call attends to).
  *   workspace    holds the plan for these arguments (psb_blockdiag_attn_plan enqueued
  *                earlier on this stream), >= psb_blockdiag_attn_bwd_workspace_size bytes,
- *                16-byte aligned.
+ *                16-byte aligned.  The plan occupies the first
+ *                psb_blockdiag_attn_fwd_workspace_size(B, Hq, Hkv, L, D) bytes and is only
+ *                read; the call writes its per-row table and key-side tile order after it.
+ *   status_word  device int32 or NULL: as in psb_blockdiag_attn_fwd (the doc_ids
+ *                precondition check, PSB_DATA_DOC_NOT_CONTIGUOUS).
  * Errors as in the forward; every bf16 pointer must be 16-byte aligned and lse
  * 4-byte aligned (PSB_ERR_INVALID_ARG).  Outputs are fp32-accumulated, rounded once
  * to bf16; P and dS are rounded to bf16 before the products that consume them.
@@ -332,7 +341,8 @@ psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, const vo
  *   lse          device fp32 [B, Hq, L] or NULL (as in psb_blockdiag_attn_fwd_lse_planned).
  *   status_word  device int32 or NULL: PSB_DATA_KV_WINDOW is OR-ed in when some row
  *                needs a key before kv_start; such rows then attend only to the keys
- *                inside the window.
+ *                inside the window.  PSB_DATA_DOC_NOT_CONTIGUOUS as in
+ *                psb_blockdiag_attn_fwd.
  * The workspace holds a plan from psb_blockdiag_attn_plan for the same doc_ids and shape
  * arguments (the plan does not depend on the window).  Everything else is as in
  * psb_blockdiag_attn_fwd_planned; with kv_start = 0 and kv_len = S the results equal it.

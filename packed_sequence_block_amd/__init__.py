@@ -30,8 +30,7 @@ from ._lib import (PAD_DOC_ID, PsbError, blockdiag_attn_bwd, blockdiag_attn_fwd,
                    validate_document_positions,
                    workspace_size)
 
-from .autograd import blockdiag_attention
-from .sdpa import (PackedState, attach_packed_varlen_hooks, blockdiag_sdpa, current_packed_state,
+from .sdpa import (PackedState, attach_packed_varlen_hooks, blockdiag_attention, blockdiag_sdpa, current_packed_state,
                    disable_packed_varlen, enable_packed_varlen, packed_documents, patched_sdpa)
 
 __all__ = ["blockdiag_attention", "PackedState", "attach_packed_varlen_hooks", "blockdiag_sdpa",

@@ -189,6 +189,8 @@ def blockdiag_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_id
     contiguous; ``doc_ids [B, S]`` int32 (global positions, -1000 = padding).
     ``scale=None`` means ``D ** -0.5``.  ``workspace`` (uint8, at least
     :func:`workspace_size` bytes) may be passed to avoid an allocation per call.
+    ``validate=True`` has the call check that every non-padding id is one run of its
+    row (through the call's status word), synchronizes and raises ``ValueError`` if not.
     """
     _need_gpu(q, k, v, doc_ids)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -209,8 +211,6 @@ def blockdiag_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_id
     ids = ids.contiguous()
     if tuple(ids.shape) != (B, S):
         raise ValueError(f"doc_ids must be [B, S] = [{B}, {S}]")
-    if validate:
-        validate_doc_ids(ids)
     if out is None:
         out = torch.empty((B, Hq, L, D), dtype=torch.bfloat16, device=q.device)
     elif out.shape != (B, Hq, L, D) or out.dtype != torch.bfloat16 or not out.is_contiguous():
@@ -221,10 +221,13 @@ def blockdiag_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_id
     sc = float(D) ** -0.5 if scale is None else float(scale)
     qs = (ctypes.c_int64 * 3)(*q.stride()[:3])
     kvs = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    word = torch.zeros(1, dtype=torch.int32, device=q.device) if validate else None
     status = load().psb_blockdiag_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(ids), B, Hq, Hkv, L, S, D, qs, kvs, int(seq_start), sc,
-        1 if enable_gqa else 0, _ptr(out), _ptr(workspace), need, None, _vp(_stream(q)))
+        1 if enable_gqa else 0, _ptr(out), _ptr(workspace), need, _ptr(word), _vp(_stream(q)))
     _check(status, "blockdiag_attn_fwd")
+    if validate and int(word.item()) & DATA_DOC_NOT_CONTIGUOUS:
+        raise ValueError("a non-padding document id occurs in more than one run of a row")
     return out
 
 

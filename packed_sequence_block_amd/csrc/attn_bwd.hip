@@ -721,7 +721,9 @@ psb_status bwd_run(const void* q, const void* k, const void* v, const void* out,
   const hipError_t e = (D == 128)
       ? launch_bwd<128>((int)nh, prm, rows, as_stream(stream))
       : launch_bwd<64>((int)nh, prm, rows, as_stream(stream));
-  return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
+  if (e != hipSuccess) return PSB_ERR_HIP;
+  // with a status word, also the precondition check the plans rely on (one launch)
+  return status != nullptr ? launch_contiguity_check(doc_ids, B, S, S, status, as_stream(stream)) : PSB_OK;
 }
 
 }  // namespace
@@ -732,9 +734,8 @@ PSB_API psb_status psb_blockdiag_attn_bwd_planned(const void* q, const void* k, 
                                                   int64_t D, int64_t seq_start, float scale, int32_t enable_gqa,
                                                   void* dq, void* dk, void* dv, void* workspace,
                                                   size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;  // no data check in this call
   return bwd_run(q, k, v, out, dout, lse, doc_ids, B, Hq, Hkv, L, S, D, seq_start, 0, S, scale, enable_gqa, dq, dk,
-                 dv, workspace, workspace_bytes, nullptr, stream);
+                 dv, workspace, workspace_bytes, status_word, stream);
 }
 
 PSB_API psb_status psb_blockdiag_attn_bwd_window_planned(const void* q, const void* k, const void* v,

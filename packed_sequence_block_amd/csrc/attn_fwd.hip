@@ -28,8 +28,8 @@
 // row's document, last valid row]; tiles entirely inside one document's causal
 // triangle for all of a wave's rows take no mask, the rest compare each key with
 // the row's [doc start, row] range.
+#include <float.h>
 #include <math.h>
-
 
 #include "attn_common.h"
 #include "psb_internal.h"
@@ -115,7 +115,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   // bytes between consecutive keys; a 64-key tile spans < 2^31 bytes (checked on the host)
   const int32_t row_bytes = (int32_t)(p.kv_ss * 2);
   const bool neg = p.sc < 0.f;
-  const float sc = neg ? -p.sc : p.sc;
+  // |scale| * log2(e), held at least at the smallest normal float.  For scale = +-0 every
+  // exp2 argument of an allowed key is then below 2^-26 in magnitude (|q.k| < 2^100), so
+  // its weight rounds to exactly 1 as scale 0 means, while a masked score (-inf) still
+  // gives exp2(-inf) = 0; with sc = 0 it would give exp2(-inf * 0) = NaN.
+  const float sc = fmaxf(neg ? -p.sc : p.sc, FLT_MIN);
   const floatx16 zero16 = {};
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
 
@@ -601,6 +605,16 @@ psb_status run_impl(const void* q, const void* k, const void* v, const int32_t* 
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }
 
+// After an attention launch that returned `st`: when the caller passed a status word,
+// also enqueue the check of the precondition the plan and the range mask rely on (each
+// non-padding id one contiguous run of its row); a split id sets
+// PSB_DATA_DOC_NOT_CONTIGUOUS.
+psb_status data_check(psb_status st, const int32_t* doc_ids, int64_t B, int64_t S, int32_t* status_word,
+                      hipStream_t s) {
+  if (st != PSB_OK || status_word == nullptr) return st;
+  return launch_contiguity_check(doc_ids, B, S, S, status_word, s);
+}
+
 }  // namespace
 }  // namespace psb
 
@@ -658,13 +672,13 @@ PSB_API psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, 
                                                   const int64_t* kv_strides, int64_t seq_start, float scale,
                                                   int32_t enable_gqa, void* out, const void* workspace,
                                                   size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;  // no data check in this call
   AttnGeometry geo;
-  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
-                  nullptr, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
+  st = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                nullptr, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
+  return data_check(st, doc_ids, B, S, status_word, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void* k, const void* v,
@@ -674,14 +688,14 @@ PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void*
                                                       int32_t enable_gqa, void* out, float* lse,
                                                       const void* workspace, size_t workspace_bytes,
                                                       int32_t* status_word, void* stream) {
-  (void)status_word;  // no data check in this call
   AttnGeometry geo;
-  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
-                  lse, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
+  st = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                lse, const_cast<void*>(workspace), workspace_bytes, nullptr, as_stream(stream));
+  return data_check(st, doc_ids, B, S, status_word, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
@@ -689,7 +703,6 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
                                           const int64_t* q_strides, const int64_t* kv_strides, int64_t seq_start,
                                           float scale, int32_t enable_gqa, void* out, void* workspace,
                                           size_t workspace_bytes, int32_t* status_word, void* stream) {
-  (void)status_word;  // no data check in this call
   AttnGeometry geo;
   psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
@@ -710,8 +723,9 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
   hipStream_t s = as_stream(stream);
   st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
   if (st != PSB_OK) return st;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
-                  nullptr, workspace, workspace_bytes, nullptr, s);
+  st = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
+                nullptr, workspace, workspace_bytes, nullptr, s);
+  return data_check(st, doc_ids, B, S, status_word, s);
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const void* k, const void* v,
@@ -731,8 +745,10 @@ PSB_API psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const vo
     return PSB_ERR_SHAPE;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return PSB_ERR_INVALID_ARG;
-  return run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, kv_start, kv_len, scale,
-                  geo, out, lse, const_cast<void*>(workspace), workspace_bytes, status_word, as_stream(stream));
+  const psb_status rs = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, kv_start,
+                                 kv_len, scale, geo, out, lse, const_cast<void*>(workspace), workspace_bytes,
+                                 status_word, as_stream(stream));
+  return data_check(rs, doc_ids, B, S, status_word, as_stream(stream));
 }
 
 PSB_API psb_status psb_masked_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* mask,

@@ -333,19 +333,28 @@ PSB_API psb_status psb_segment_cu_seqlens(const int32_t* doc_ids_row, int64_t se
   return PSB_OK;
 }
 
-PSB_API psb_status psb_validate_doc_ids(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
-                                        int32_t* status_word, void* stream) {
-  if (B < 0 || S < 0 || status_word == nullptr) return PSB_ERR_INVALID_ARG;
+namespace psb {
+
+psb_status launch_contiguity_check(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
+                                   int32_t* status_word, hipStream_t stream) {
   if (B == 0 || S == 0) return PSB_OK;
-  if (doc_ids == nullptr) return PSB_ERR_INVALID_ARG;
+  if (doc_ids == nullptr || status_word == nullptr) return PSB_ERR_INVALID_ARG;
   if (row_stride < S || S >= INT32_MAX) return PSB_ERR_SHAPE;
   const int64_t waves = B * S;
   const int64_t blocks = ceil_div(waves, 256 / kWave);
   if (blocks >= INT32_MAX) return PSB_ERR_SHAPE;
-  contiguity_kernel<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(doc_ids, B, (int32_t)S,
-                                                                                  row_stride, status_word);
+  contiguity_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(doc_ids, B, (int32_t)S, row_stride,
+                                                                      status_word);
   PSB_LAUNCH_CHECK();
   return PSB_OK;
+}
+
+}  // namespace psb
+
+PSB_API psb_status psb_validate_doc_ids(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
+                                        int32_t* status_word, void* stream) {
+  if (B < 0 || S < 0 || status_word == nullptr) return PSB_ERR_INVALID_ARG;
+  return launch_contiguity_check(doc_ids, B, S, row_stride, status_word, as_stream(stream));
 }
 
 PSB_API psb_status psb_doc_ids_from_seq_lens(const int32_t* seq_lens, int64_t B, int64_t n_docs, int64_t seq_len,

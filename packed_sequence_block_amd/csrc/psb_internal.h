@@ -33,4 +33,10 @@ __device__ inline int32_t last_le(const int32_t* c, int32_t n, int32_t p) {
   return lo - 1;
 }
 
+// Enqueues the check that every non-padding id of doc_ids [B, S] (row stride row_stride)
+// forms one contiguous run per row; ORs PSB_DATA_DOC_NOT_CONTIGUOUS into *status_word
+// when not.  Argument errors are returned before anything is enqueued.
+psb_status launch_contiguity_check(const int32_t* doc_ids, int64_t B, int64_t S, int64_t row_stride,
+                                   int32_t* status_word, hipStream_t stream);
+
 }  // namespace psb

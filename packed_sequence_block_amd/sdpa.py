@@ -56,8 +56,15 @@ def blockdiag_attn_bwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out
                           dout: torch.Tensor, lse: torch.Tensor, doc_ids: torch.Tensor, workspace: torch.Tensor,
                           seq_start: int, scale: float, enable_gqa: bool
                           ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    # The library's backward writes its per-row table and key-side tile order after the
+    # plan (the first workspace_size bytes).  It gets a fresh buffer holding a copy of the
+    # plan, so the forward's saved workspace is never written and the op mutates nothing.
+    B, Hq, L, D = q.shape
+    n = _lib.workspace_size(B, Hq, k.shape[1], L, D)
+    ws = torch.empty_like(workspace)
+    ws[:n].copy_(workspace[:n])
     return _lib.blockdiag_attn_bwd(q.contiguous(), k.contiguous(), v.contiguous(), out,
-                                   dout.to(torch.bfloat16).contiguous(), lse, doc_ids, workspace, seq_start, scale,
+                                   dout.to(torch.bfloat16).contiguous(), lse, doc_ids, ws, seq_start, scale,
                                    enable_gqa)
 
 
@@ -84,6 +91,17 @@ def _backward(ctx, dout, dlse, dws):
 
 
 blockdiag_attn_fwd_op.register_autograd(_backward, setup_context=_setup_context)
+
+
+def blockdiag_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, doc_ids: torch.Tensor,
+                        seq_start: int = 0, scale: float | None = None, enable_gqa: bool = False) -> torch.Tensor:
+    """Differentiable block-diagonal (per-document causal) attention, ``[B, Hq, L, D]`` bf16,
+    with explicit document ids ``[B, S]`` (no armed state).  For a query shard the k / v
+    gradients are the shard's own contributions, which the caller sums across ranks (the
+    glm5_next.cp page's differentiable gathers route them back the same way)."""
+    sc = float(q.shape[-1]) ** -0.5 if scale is None else float(scale)
+    out, _, _ = blockdiag_attn_fwd_op(q, k, v, doc_ids, int(seq_start), sc, bool(enable_gqa))
+    return out
 
 
 def _ids_2d(doc_ids: torch.Tensor, B: int) -> torch.Tensor:

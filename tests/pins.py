@@ -122,6 +122,26 @@ def pin_zero_query_prefix_mean(attn):
     _close(out[0, 0], ref)
 
 
+def pin_zero_scale_prefix_mean(attn):
+    """scale = 0 (either sign) with arbitrary q: every allowed score is 0, so a row is
+    again the plain mean of V over ``[doc_start, qpos]``, with padding rows 0."""
+    lens, pad = [6, 1, 9], 3
+    S = sum(lens) + pad
+    D = 4
+    q, k, v = _bf16_randn((1, 2, S, D), 911), _bf16_randn((1, 1, S, D), 912), _bf16_randn((1, 1, S, D), 913)
+    ref = torch.zeros((S, D), dtype=torch.float64)
+    a = 0
+    vv = v[0, 0].double()
+    for n in lens:
+        cs = torch.cumsum(vv[a:a + n], dim=0)
+        ref[a:a + n] = cs / torch.arange(1, n + 1, dtype=torch.float64).unsqueeze(1)
+        a += n
+    for sc in (0.0, -0.0):
+        out = torch.as_tensor(np.asarray(attn(q, k, v, _ids(lens, pad), 0, sc, True)))
+        _close(out[0, 0], ref)
+        _close(out[0, 1], ref)
+
+
 def pin_constant_value_per_document(attn):
     """V constant inside each document => output equals that constant."""
     lens = [5, 8, 3]
@@ -165,5 +185,6 @@ def pin_hand_example(attn, golden):
 
 
 ALL_PINS = [pin_single_document, pin_packed_equals_per_document, pin_shard_equals_rows,
-            pin_padding_rows_zero, pin_zero_query_prefix_mean, pin_constant_value_per_document,
+            pin_padding_rows_zero, pin_zero_query_prefix_mean, pin_zero_scale_prefix_mean,
+            pin_constant_value_per_document,
             pin_gqa_equals_repeat_interleave]

@@ -94,3 +94,35 @@ def test_opcheck_custom_op(psb):
     say("opcheck")
     torch.library.opcheck(torch.ops.psb.blockdiag_attn_fwd.default, args,
                           test_utils=("test_schema", "test_autograd_registration", "test_faketensor"))
+
+
+def test_opcheck_backward_op(psb):
+    lay, q, k, v, ids = _case(55)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda()
+    out, lse, ws = torch.ops.psb.blockdiag_attn_fwd(qd, kd, vd, idd, 0, 64 ** -0.5, True)
+    g = torch.Generator().manual_seed(56)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+    args = (qd, kd, vd, out, dout, lse, idd, ws, 0, 64 ** -0.5, True)
+    say("opcheck backward op")
+    torch.library.opcheck(torch.ops.psb.blockdiag_attn_bwd.default, args,
+                          test_utils=("test_schema", "test_faketensor"))
+
+
+def test_backward_twice_leaves_saved_workspace_intact(psb):
+    # retain_graph: the second backward reads the same saved plan and gives the same grads
+    lay, q, k, v, ids = _case(57)
+    qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    g = torch.Generator().manual_seed(58)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+    say("backward twice")
+    with psb.packed_documents(torch.as_tensor(ids).cuda()):
+        out = psb.blockdiag_sdpa(qd, kd, vd, enable_gqa=True)
+    out.backward(dout, retain_graph=True)
+    first = [t.grad.clone() for t in (qd, kd, vd)]
+    for t in (qd, kd, vd):
+        t.grad = None
+    out.backward(dout)
+    torch.cuda.synchronize()
+    for a, t in zip(first, (qd, kd, vd)):
+        assert torch.equal(a, t.grad)

@@ -139,6 +139,8 @@ WRAPPED = {
     "k_v_swapped": lambda q, k, v, ids, s0, sc, g: _oracle(q, v, k, ids, s0, sc, g),
     "scale_ignored": lambda q, k, v, ids, s0, sc, g: _oracle(q, k, v, ids, s0, 1.0, g),
     "shard_offset_ignored": lambda q, k, v, ids, s0, sc, g: _oracle(q, k, v, ids, 0, sc, g),
+    # a falsy test on the scale turns 0 into the default D ** -0.5
+    "zero_scale_as_default": lambda q, k, v, ids, s0, sc, g: _oracle(q, k, v, ids, s0, sc or None, g),
 }
 
 
