@@ -41,6 +41,7 @@ typedef int32_t psb_status;
 #define PSB_ERR_UNSUPPORTED (-3) /* head dim other than 64 or 128 */
 #define PSB_ERR_CAPACITY (-4)    /* output or workspace buffer too small */
 #define PSB_ERR_HIP (-5)         /* a HIP runtime call failed (e.g. launch) */
+#define PSB_ERR_SCRATCH_LIMIT (-6) /* no-allocation call: plan tables exceed its static buffer */
 
 #define PSB_PAD_DOC_ID (-1000)
 
@@ -208,6 +209,30 @@ psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v,
                                   const int64_t* kv_strides, int64_t seq_start, float scale,
                                   int32_t enable_gqa, void* out, void* workspace,
                                   size_t workspace_bytes, int32_t* status_word, void* stream);
+
+/*
+ * psb_blockdiag_attn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the scheduler tables live in a static device array of the library, one per
+ * GPU, of psb_blockdiag_attn_fwd_noalloc_max_workspace() bytes (4 MiB), held until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ * Arguments, outputs, status_word and errors as in psb_blockdiag_attn_fwd (the stream must
+ * belong to the current device), plus PSB_ERR_SCRATCH_LIMIT, returned before anything is
+ * enqueued, when the problem's tables need more than the static array holds, i.e. when
+ * psb_blockdiag_attn_fwd_workspace_size(B, Hq, Hkv, L, D) exceeds it (about
+ * 4 MiB / 72 bytes = 58000 32-row query blocks over all rows; B * L up to 1.8M rows).
+ * Every call on one GPU uses that GPU's array: calls that overlap in time on one GPU
+ * (on different streams or from different threads without ordering) race and give
+ * wrong outputs.  The array needs no clearing: each call's plan rewrites every entry the
+ * attention kernel reads.
+ */
+size_t psb_blockdiag_attn_fwd_noalloc_max_workspace(void);
+psb_status psb_blockdiag_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                          const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                          int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                          const int64_t* kv_strides, int64_t seq_start, float scale,
+                                          int32_t enable_gqa, void* out, int32_t* status_word, void* stream);
 
 /*
  * The two halves of psb_blockdiag_attn_fwd, for callers that run many

@@ -21,6 +21,7 @@ PSB_ERR_SHAPE = -2
 PSB_ERR_UNSUPPORTED = -3
 PSB_ERR_CAPACITY = -4
 PSB_ERR_HIP = -5
+PSB_ERR_SCRATCH_LIMIT = -6
 PAD_DOC_ID = -1000
 DATA_CU_NOT_MONOTONE = 1
 DATA_CU_OUT_OF_RANGE = 2
@@ -61,6 +62,9 @@ SIGNATURES = {
     "psb_blockdiag_attn_fwd": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, ctypes.c_size_t,
                                         _vp, _vp]),
+    "psb_blockdiag_attn_fwd_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "psb_blockdiag_attn_fwd_noalloc": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                _vp, _vp, _c_i64, ctypes.c_float, _c_i32, _vp, _vp, _vp]),
     "psb_blockdiag_attn_plan": (_c_i32, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32,
                                          _vp, ctypes.c_size_t, _vp]),
     "psb_blockdiag_attn_fwd_planned": (_c_i32, [_vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,

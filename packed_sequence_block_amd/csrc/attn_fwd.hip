@@ -31,6 +31,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "attn_common.h"
 #include "psb_internal.h"
 #include "schedule.h"
@@ -698,11 +700,15 @@ PSB_API psb_status psb_blockdiag_attn_fwd_lse_planned(const void* q, const void*
   return data_check(st, doc_ids, B, S, status_word, as_stream(stream));
 }
 
-PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
-                                          int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S, int64_t D,
-                                          const int64_t* q_strides, const int64_t* kv_strides, int64_t seq_start,
-                                          float scale, int32_t enable_gqa, void* out, void* workspace,
-                                          size_t workspace_bytes, int32_t* status_word, void* stream) {
+namespace psb {
+namespace {
+
+// Plan + attention (+ the precondition check with a status word) into `workspace`; every
+// argument is checked before anything is enqueued.
+psb_status fwd_whole(const void* q, const void* k, const void* v, const int32_t* doc_ids, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                     const int64_t* kv_strides, int64_t seq_start, float scale, int32_t enable_gqa, void* out,
+                     void* workspace, size_t workspace_bytes, int32_t* status_word, hipStream_t s) {
   AttnGeometry geo;
   psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
@@ -720,12 +726,77 @@ PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const vo
   if (qs[2] < D || kvs[2] < D) return PSB_ERR_SHAPE;
   if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PSB_ERR_INVALID_ARG;
-  hipStream_t s = as_stream(stream);
   st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
   if (st != PSB_OK) return st;
   st = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
                 nullptr, workspace, workspace_bytes, nullptr, s);
   return data_check(st, doc_ids, B, S, status_word, s);
+}
+
+}  // namespace
+}  // namespace psb
+
+PSB_API psb_status psb_blockdiag_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
+                                          int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S, int64_t D,
+                                          const int64_t* q_strides, const int64_t* kv_strides, int64_t seq_start,
+                                          float scale, int32_t enable_gqa, void* out, void* workspace,
+                                          size_t workspace_bytes, int32_t* status_word, void* stream) {
+  return fwd_whole(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, enable_gqa, out,
+                   workspace, workspace_bytes, status_word, as_stream(stream));
+}
+
+// ---- no-allocation variant ---------------------------------------------------------------
+// The scheduler tables of psb_blockdiag_attn_fwd_noalloc live in this static device array:
+// every GPU the library runs on holds one copy (kScratchBytes) until the process ends.  In
+// host code `scratch` names a host-side stand-in, never device memory: the host uses only the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace psb {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+psb_status scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PSB_ERR_HIP;
+  if (dev >= kMaxDevices) return PSB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PSB_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PSB_OK;
+}
+
+}  // namespace
+}  // namespace psb
+
+PSB_API size_t psb_blockdiag_attn_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+PSB_API psb_status psb_blockdiag_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                                  const int32_t* doc_ids, int64_t B, int64_t Hq, int64_t Hkv,
+                                                  int64_t L, int64_t S, int64_t D, const int64_t* q_strides,
+                                                  const int64_t* kv_strides, int64_t seq_start, float scale,
+                                                  int32_t enable_gqa, void* out, int32_t* status_word,
+                                                  void* stream) {
+  AttnGeometry geo;
+  const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
+  if (st != PSB_OK) return st;
+  if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
+  // the plan tables must fit the static array: larger problems are refused, never truncated
+  if ((size_t)schedule_bytes(B, L, geo.nr) > kScratchBytes) return PSB_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const psb_status sa = scratch_address(&ws);
+  if (sa != PSB_OK) return sa;
+  return fwd_whole(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, scale, enable_gqa, out,
+                   ws, kScratchBytes, status_word, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd_window_planned(const void* q, const void* k, const void* v,

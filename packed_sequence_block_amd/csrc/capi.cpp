@@ -11,6 +11,8 @@ PSB_API const char* psb_status_string(psb_status status) {
     case PSB_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are built)";
     case PSB_ERR_CAPACITY: return "output or workspace buffer too small";
     case PSB_ERR_HIP: return "HIP runtime error (kernel launch failed)";
+    case PSB_ERR_SCRATCH_LIMIT:
+      return "problem needs more scheduler memory than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }
