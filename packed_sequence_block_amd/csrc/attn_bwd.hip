@@ -67,7 +67,20 @@ struct BwdParams {
   int32_t nkt;              // key tiles per batch row
   int32_t kv_start, kv_len;
   int32_t* status;          // PSB_DATA_KV_WINDOW when a row needs a key before kv_start, or null
+  int32_t nrec;             // key-side records (the dK / dV grid covers nrec x Hkv items)
+  int32_t max_slots;        // partial slots in `partial`
+  float* partial;           // fp32 partial dK / dV of the chunks of split key tiles
+  const int32_t* split;     // split key tiles {b, key tile, first slot, chunks}
+  const int32_t* split_n;   // their number
 };
+
+// fp32 partials of one (slot, kv head): per wave, dK then dV accumulators in MFMA order,
+// as float4 [2][DB][4][64 lanes] (each store instruction writes 1 KiB)
+template <int D>
+__device__ __forceinline__ float4* partial_at(float* base, int32_t slot, int32_t Hkv, int32_t g, int wv) {
+  constexpr int64_t per_wave = 2 * (D / 32) * 16 * 64;  // floats
+  return reinterpret_cast<float4*>(base + (((int64_t)slot * Hkv + g) * kBwdWaves + wv) * per_wave);
+}
 
 // ---- dQ: query-stationary ---------------------------------------------------------
 template <int D, int NH>
@@ -288,10 +301,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 // k <= r < end(k), end(k) = one past the last position of k's document (a padding key
 // has no rows).  Rows are local query rows [0, L) at global positions seq_start + r.
 template <int D>
-__global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
-  // query rows per step: 64 (two independent 32-row halves) at D = 128, where the extra
-  // independent MFMA work pays; 32 at D = 64, where it did not (measured)
-  constexpr int kRowsPerStep = (D == 128) ? 64 : 32;
+__global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
+  // 32 query rows per step, two waves per SIMD.  At D = 128 a wave's V rows wait in LDS
+  // (its own 32 rows, read back as the dP MFMA operand) instead of 32 VGPRs, which keeps
+  // the wave within 256 registers next to its 128 dK / dV accumulators.
+  constexpr int kRowsPerStep = 32;
+  constexpr bool VLDS = D == 128;
+  constexpr int VROW = D + 8;  // padded V row: the 16 rows of one b128 read on distinct banks
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
@@ -305,6 +321,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sQ1[QSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sO0[QSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sO1[QSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[VLDS ? kKeysPerItem * VROW : 8];
   __shared__ __attribute__((aligned(16))) float sL[2][kRowsPerStep];   // per row: lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sDl[2][kRowsPerStep];  // per row: delta
   __shared__ int32_t s_rng[kBwdWaves][2];
@@ -331,11 +348,15 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
 
   // item = key-tile rank x kv head; kv head = item % Hkv keeps (with 8 kv heads) one kv
   // head per XCD
-  for (int64_t item = blockIdx.x; item < (int64_t)p.B * p.Hkv * nkt; item += gridDim.x) {
+  for (int64_t item = blockIdx.x; item < (int64_t)p.nrec * p.Hkv; item += gridDim.x) {
     const TileRecord& rec = p.kwork[item / p.Hkv];
     const int32_t g = (int32_t)(item % p.Hkv);
     const int32_t b = rec.b, kt_i = rec.rt;
-    if (b < 0 || b >= p.B || kt_i < 0 || kt_i >= nkt) continue;  // workspace from another plan
+    // empty records, and records a plan for this shape cannot have written
+    if (b < 0 || b >= p.B || kt_i < 0 || kt_i >= nkt) continue;
+    // a chunk of a split tile: rows [rec.lo, rec.hi) only, into partial slot rec.blk_lo[0]
+    const int32_t slot = rec.blk_lo[0], nchunks = rec.blk_lo[2];
+    const bool chunked = nchunks > 1 && slot >= 0 && slot < p.max_slots;
     const int32_t key = p.kv_start + kt_i * kKeysPerItem + kKeysPerWave * wv + lr;  // global position
     const bool key_in = key < p.kv_start + p.kv_len;
     const int32_t* docrow = p.doc + (int64_t)b * p.S;
@@ -382,6 +403,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     // local rows [r_lo, r_hi) that see this key
     int32_t r_lo = key_valid ? max(key, p.seq_start) - p.seq_start : 0;
     int32_t r_hi = key_valid ? min(kend, p.seq_start + p.L) - p.seq_start : 0;
+    if (chunked) {  // this chunk's rows only: each row is counted by exactly one chunk
+      r_lo = max(r_lo, rec.lo);
+      r_hi = min(r_hi, rec.hi);
+    }
     if (r_hi < r_lo) r_hi = r_lo;
     // wave range: min / max over its keys (empty keys excluded)
     {
@@ -403,6 +428,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
 
     // ---- stationary K^T and V^T operands (B operands: lane = key) --------------------------
     bf16x8 kreg[KS], vreg[KS];
+    // this lane's V row in the wave's own LDS rows (VLDS): written and read by this wave only
+    const int v_rd = (kKeysPerWave * wv + lr) * VROW + 8 * h;
     {
       const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
 #pragma unroll
@@ -414,6 +441,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) { kreg[ks][t] = (__bf16)0.f; vreg[ks][t] = (__bf16)0.f; }
         }
+        if constexpr (VLDS) *(bf16x8*)(sV + v_rd + 16 * ks) = vreg[ks];
       }
     }
     floatx16 dka[DB], dva[DB];
@@ -503,7 +531,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
           const bf16x8 aq = *(const bf16x8*)(qb + a_rd + 32 * hf * QROW + 16 * ks);
           const bf16x8 ao = *(const bf16x8*)(ob + a_rd + 32 * hf * QROW + 16 * ks);
           s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
-          dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[hf], 0, 0, 0);
+          const bf16x8 bv = VLDS ? *(const bf16x8*)(sV + v_rd + 16 * ks) : vreg[ks];
+          dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, dp[hf], 0, 0, 0);
         }
         constexpr int EVERY = (KS / QFULL >= 1) ? KS / QFULL : 1;
         if (SPREAD && (ks % EVERY) == EVERY - 1 && ks / EVERY < QFULL) {
@@ -587,8 +616,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
     }
     if (st < nsteps) step(st, sQ0, sO0, sQ1, sO1, 0);
 
-    // ---- epilogue: C[d][key] -> dk, dv rows (lane = key) ------------------------------------
-    {
+    // ---- epilogue: C[d][key] -> dk, dv rows (lane = key), or the chunk's fp32 partial -------
+    if (chunked) {
+      float4* pp = partial_at<D>(p.partial, slot, p.Hkv, g, wv);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          pp[((0 * DB + db) * 4 + i4) * 64 + lane] =
+              make_float4(dka[db][4 * i4], dka[db][4 * i4 + 1], dka[db][4 * i4 + 2], dka[db][4 * i4 + 3]);
+          pp[((1 * DB + db) * 4 + i4) * 64 + lane] =
+              make_float4(dva[db][4 * i4], dva[db][4 * i4 + 1], dva[db][4 * i4 + 2], dva[db][4 * i4 + 3]);
+        }
+    } else {
       const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
       __bf16* dkr = p.dk + kvrow * D;
       __bf16* dvr = p.dv + kvrow * D;
@@ -598,6 +638,46 @@ __global__ void __launch_bounds__(kBwdThreads, 1) dkdv_kernel(BwdParams p) {
         store_block_bf16(dvr + 32 * db, dva[db], 1.f, key_in, h);
       }
     }
+  }
+}
+
+// ---- dK, dV of split key tiles: the chunks' partials summed in chunk order -------------
+// Workgroup = (split tile, kv head), the dK / dV kernel's lane layout; grid covers the most
+// split tiles a plan can make, the rest exit.
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) dkdv_reduce_kernel(BwdParams p) {
+  constexpr int DB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, lr = lane & 31;
+  const int32_t i = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+  if (i >= *p.split_n) return;
+  const int32_t b = p.split[4 * i], kt_i = p.split[4 * i + 1], slot0 = p.split[4 * i + 2], n = p.split[4 * i + 3];
+  if (b < 0 || b >= p.B || kt_i < 0 || slot0 < 0 || n < 2 || n > p.max_slots || slot0 > p.max_slots - n) return;
+  floatx16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) { dka[db] = floatx16{}; dva[db] = floatx16{}; }
+  for (int32_t j = 0; j < n; ++j) {
+    const float4* pp = partial_at<D>(p.partial, slot0 + j, p.Hkv, g, wv);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 a = pp[((0 * DB + db) * 4 + i4) * 64 + lane];
+        const float4 c = pp[((1 * DB + db) * 4 + i4) * 64 + lane];
+        dka[db][4 * i4] += a.x; dka[db][4 * i4 + 1] += a.y; dka[db][4 * i4 + 2] += a.z; dka[db][4 * i4 + 3] += a.w;
+        dva[db][4 * i4] += c.x; dva[db][4 * i4 + 1] += c.y; dva[db][4 * i4 + 2] += c.z; dva[db][4 * i4 + 3] += c.w;
+      }
+  }
+  const int32_t key = p.kv_start + kt_i * kKeysPerItem + kKeysPerWave * wv + lr;
+  const bool key_in = key < p.kv_start + p.kv_len;
+  const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
+  __bf16* dkr = p.dk + kvrow * D;
+  __bf16* dvr = p.dv + kvrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    store_block_bf16(dkr + 32 * db, dka[db], p.scale, key_in, h);
+    store_block_bf16(dvr + 32 * db, dva[db], 1.f, key_in, h);
   }
 }
 
@@ -626,9 +706,12 @@ hipError_t launch_bwd(int nh, const BwdParams& prm, int64_t rows, hipStream_t s)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t kgrid = (int64_t)prm.B * prm.Hkv * ((prm.kv_len + kKeysPerItem - 1) / kKeysPerItem);
+  const int64_t kgrid = (int64_t)prm.nrec * prm.Hkv;
   if (kgrid == 0) return hipSuccess;
   dkdv_kernel<D><<<dim3((unsigned)kgrid), dim3(kBwdThreads), 0, s>>>(prm);
+  e = hipGetLastError();
+  if (e != hipSuccess || prm.max_slots < 2) return e;
+  dkdv_reduce_kernel<D><<<dim3((unsigned)(prm.max_slots / 2 * prm.Hkv)), dim3(kBwdThreads), 0, s>>>(prm);
   return hipGetLastError();
 }
 
@@ -639,9 +722,8 @@ using namespace psb;
 
 PSB_API size_t psb_blockdiag_attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t S,
                                                      int64_t D) {
-  (void)D;
-  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0) return 256;
-  return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L) + key_schedule_bytes(B, S));
+  if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || (D != 64 && D != 128)) return 256;
+  return (size_t)(bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L) + key_schedule_bytes(B, S, Hkv, D));
 }
 
 namespace {
@@ -679,15 +761,14 @@ psb_status bwd_run(const void* q, const void* k, const void* v, const void* out,
   const int64_t nr = kBwdWaves / nh;
   const int64_t ntiles = (L > 0) ? schedule_ntiles(B, L, nr) : 0;
   const int64_t units = Hq / nh;
-  if (ntiles * units >= INT32_MAX || B * Hkv * ((kv_len + kKeysPerItem - 1) / kKeysPerItem) >= INT32_MAX)
+  if (ntiles * units >= INT32_MAX ||
+      (B * ((kv_len + kKeysPerItem - 1) / kKeysPerItem) + key_max_slots(B, S, Hkv, D)) * Hkv >= INT32_MAX)
     return PSB_ERR_SHAPE;
   const ScheduleBuffers buf = schedule_carve(workspace, B, L, nr);
   char* wsb = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(wsb + bwd_plan_bytes(B, Hq, Hkv, L));
-  char* kss = wsb + bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L);
-  int32_t* klo = reinterpret_cast<int32_t*>(kss);
-  int32_t* khi = reinterpret_cast<int32_t*>(kss + pad256(4 * key_ntiles(B, S)));
-  TileRecord* kwork = reinterpret_cast<TileRecord*>(kss + 2 * pad256(4 * key_ntiles(B, S)));
+  const KeySchedule ks =
+      key_schedule_carve(wsb + bwd_plan_bytes(B, Hq, Hkv, L) + bwd_delta_bytes(B, Hq, L), B, S, Hkv, D, kv_len);
   BwdParams prm;
   prm.q = static_cast<const __bf16*>(q);
   prm.k = static_cast<const __bf16*>(k);
@@ -709,14 +790,19 @@ psb_status bwd_run(const void* q, const void* k, const void* v, const void* out,
   prm.sc = fabsf(scale) * kLog2e;
   prm.items = ntiles * units;
   prm.work = buf.work;
-  prm.kwork = kwork;
+  prm.kwork = ks.work;
+  prm.nrec = ks.nrec;
+  prm.max_slots = ks.max_slots;
+  prm.partial = ks.partial;
+  prm.split = ks.split;
+  prm.split_n = ks.split_n;
   prm.nkt = (int32_t)((kv_len + kKeyTile - 1) / kKeyTile);
   prm.kv_start = (int32_t)kv_start;
   prm.kv_len = (int32_t)kv_len;
   prm.status = status;
   const int64_t rows = B * Hq * L;
   if (launch_key_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, (int32_t)kv_start,
-                          (int32_t)kv_len, klo, khi, kwork, as_stream(stream)) != hipSuccess)
+                          (int32_t)kv_len, (int32_t)Hkv, ks, as_stream(stream)) != hipSuccess)
     return PSB_ERR_HIP;
   const hipError_t e = (D == 128)
       ? launch_bwd<128>((int)nh, prm, rows, as_stream(stream))

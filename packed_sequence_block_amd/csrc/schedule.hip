@@ -92,24 +92,14 @@ __device__ inline TileRecord make_record(const int32_t* __restrict__ blk_lo, con
   return r;
 }
 
-// Records of all B * ntile_row row tiles into work[], longest key range first: a counting
-// sort over the tile count of each record's range (bucket kBuckets - 1 collects the
-// rest), done by one workgroup of NT threads.  hist: kBuckets ints of LDS, wsum: NT / 64.
+// Turns the bucket counts hist[kBuckets] into exclusive offsets in DESCENDING bucket
+// order (offset(bk) = sum of the counts of the buckets above bk), with one workgroup of NT
+// threads; ends with a barrier.  wsum: NT / 64 ints of LDS.
 template <int NT>
-__device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_t B, int32_t nblk, int32_t nr,
-                            int32_t ntile_row, TileRecord* __restrict__ work, int32_t* hist, int32_t* wsum) {
+__device__ void bucket_offsets_desc(int32_t* hist, int32_t* wsum) {
   static_assert(kBuckets % NT == 0, "buckets split evenly over the threads");
   constexpr int PER = kBuckets / NT;  // consecutive buckets (in descending order) per thread
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-  const int32_t T = B * ntile_row;
-  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
-  __syncthreads();
-  for (int32_t t = tid; t < T; t += NT) {
-    const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
-    atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
-  }
-  __syncthreads();
-  // exclusive scan in DESCENDING bucket order: offset(bk) = sum of hist[bk' > bk]
   int32_t c[PER];
   int32_t own = 0;
 #pragma unroll
@@ -134,6 +124,24 @@ __device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_
     run += c[k];
   }
   __syncthreads();
+}
+
+// Records of all B * ntile_row row tiles into work[], longest key range first: a counting
+// sort over the tile count of each record's range (bucket kBuckets - 1 collects the
+// rest), done by one workgroup of NT threads.  hist: kBuckets ints of LDS, wsum: NT / 64.
+template <int NT>
+__device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_t B, int32_t nblk, int32_t nr,
+                            int32_t ntile_row, TileRecord* __restrict__ work, int32_t* hist, int32_t* wsum) {
+  const int tid = threadIdx.x;
+  const int32_t T = B * ntile_row;
+  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (int32_t t = tid; t < T; t += NT) {
+    const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
+    atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
+  }
+  __syncthreads();
+  bucket_offsets_desc<NT>(hist, wsum);
   for (int32_t t = tid; t < T; t += NT) {
     const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
     const int32_t bk = min(tile_iters(r.lo, r.hi), kBuckets - 1);
@@ -200,6 +208,131 @@ __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restric
     klo[wid] = (r1 > r0) ? r0 - seq_start : 0;
     khi[wid] = (r1 > r0) ? r1 - seq_start : 0;
   }
+}
+
+// Key-side plan (one workgroup): splits key tiles whose row range is far longer than a
+// workgroup slot's balanced share into row chunks and orders all records longest first.
+//   * W = total rows over all tiles; a record of r rows costs r x group per workgroup and
+//     there are B * nkt x Hkv workgroups' worth of records over kKeySlots concurrent slots
+//     (two workgroups on each of 256 CUs), so the chunk length is
+//     Rc = max(kMinChunkRows, W * Hkv / kKeySlots rounded up to 32 rows);
+//   * a tile of len > Rc rows would take n = ceil(len / Rc) chunks (at most kMaxChunks);
+//     partial slots go to the tiles with the most chunks first, as long as the slot budget
+//     lasts; a tile that gets none stays one record;
+//   * records are counting-sorted by ceil(rows / 64), descending.
+constexpr int kKeyPlanThreads = 1024;
+constexpr int kKeySlots = 512;
+constexpr int kMinChunkRows = 256;
+constexpr int kMaxChunks = 16;
+
+__device__ inline int32_t chunks_of(int32_t len, int32_t rc) {
+  return len > rc ? min((len + rc - 1) / rc, kMaxChunks) : 1;
+}
+
+// chunk j of a tile with rows [lo, hi) in n chunks of rc rows (the last one shorter)
+__device__ inline TileRecord key_record(int32_t b, int32_t kt, int32_t lo, int32_t hi, int32_t n, int32_t j,
+                                        int32_t rc, int32_t slot) {
+  TileRecord r;
+  r.b = b;
+  r.rt = kt;
+  r.lo = (n > 1) ? lo + j * rc : lo;
+  r.hi = (n > 1) ? min(hi, lo + (j + 1) * rc) : hi;
+  r.blk_lo[0] = (slot >= 0) ? slot + j : -1;
+  r.blk_lo[1] = j;
+  r.blk_lo[2] = n;
+  r.blk_lo[3] = 0;
+  r.blk_hi[0] = r.blk_hi[1] = r.blk_hi[2] = r.blk_hi[3] = 0;
+  r.pad[0] = r.pad[1] = r.pad[2] = r.pad[3] = 0;
+  return r;
+}
+
+__global__ void __launch_bounds__(kKeyPlanThreads) key_plan_kernel(
+    const int32_t* __restrict__ klo, const int32_t* __restrict__ khi, int32_t B, int32_t nkt, int32_t Hkv,
+    int32_t max_slots, int32_t nrec, int32_t* __restrict__ tslot, TileRecord* __restrict__ work,
+    int32_t* __restrict__ split, int32_t* __restrict__ split_n) {
+  constexpr int NT = kKeyPlanThreads;
+  __shared__ int32_t hist[kBuckets];
+  __shared__ int32_t wsum[NT / kWave];
+  __shared__ unsigned long long s_total;
+  __shared__ int32_t s_rc, s_nsplit, s_nrec;
+  __shared__ int32_t cnt[kMaxChunks + 1], take[kMaxChunks + 1], base[kMaxChunks + 1], ticket[kMaxChunks + 1];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int32_t T = B * nkt;
+  if (tid == 0) { s_total = 0ull; s_nsplit = 0; s_nrec = 0; }
+  if (tid <= kMaxChunks) { cnt[tid] = 0; take[tid] = 0; base[tid] = 0; ticket[tid] = 0; }
+  for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
+  __syncthreads();
+  unsigned long long part = 0ull;
+  for (int32_t t = tid; t < T; t += NT) part += (unsigned long long)max(0, khi[t] - klo[t]);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) part += __shfl_xor(part, off, kWave);
+  if (lane == 0) atomicAdd(&s_total, part);
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long rc = (s_total * (unsigned long long)Hkv + kKeySlots - 1) / kKeySlots;
+    rc = (rc + 31ull) / 32ull * 32ull;
+    if (rc < (unsigned long long)kMinChunkRows) rc = kMinChunkRows;
+    s_rc = (int32_t)min(rc, (unsigned long long)0x40000000);
+  }
+  __syncthreads();
+  const int32_t rc = s_rc;
+  for (int32_t t = tid; t < T; t += NT) {
+    const int32_t n = chunks_of(max(0, khi[t] - klo[t]), rc);
+    if (n >= 2) atomicAdd(&cnt[n], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {  // the slot budget, tiles with the most chunks first
+    int32_t used = 0;
+    for (int n = kMaxChunks; n >= 2; --n) {
+      const int32_t k = min(cnt[n], (max_slots - used) / n);
+      take[n] = k;
+      base[n] = used;
+      used += k * n;
+    }
+  }
+  __syncthreads();
+  for (int32_t t = tid; t < T; t += NT) {
+    const int32_t n = chunks_of(max(0, khi[t] - klo[t]), rc);
+    int32_t sl = -1;
+    if (n >= 2) {
+      const int32_t tk = atomicAdd(&ticket[n], 1);
+      if (tk < take[n]) sl = base[n] + tk * n;
+    }
+    tslot[t] = sl;
+    if (sl >= 0) {
+      const int32_t i = atomicAdd(&s_nsplit, 1);
+      split[4 * i + 0] = t / nkt;
+      split[4 * i + 1] = t % nkt;
+      split[4 * i + 2] = sl;
+      split[4 * i + 3] = n;
+    }
+  }
+  __syncthreads();  // tslot written by other threads of this workgroup is visible after this
+  // records: histogram of lengths, descending offsets, scatter
+  for (int32_t t = tid; t < T; t += NT) {
+    const int32_t lo = klo[t], hi = khi[t], sl = tslot[t];
+    const int32_t n = (sl >= 0) ? chunks_of(hi - lo, rc) : 1;
+    for (int32_t j = 0; j < n; ++j) {
+      const TileRecord r = key_record(t / nkt, t % nkt, lo, hi, n, j, rc, sl);
+      atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
+    }
+    atomicAdd(&s_nrec, n);
+  }
+  __syncthreads();
+  bucket_offsets_desc<NT>(hist, wsum);
+  for (int32_t t = tid; t < T; t += NT) {
+    const int32_t lo = klo[t], hi = khi[t], sl = tslot[t];
+    const int32_t n = (sl >= 0) ? chunks_of(hi - lo, rc) : 1;
+    for (int32_t j = 0; j < n; ++j) {
+      const TileRecord r = key_record(t / nkt, t % nkt, lo, hi, n, j, rc, sl);
+      work[atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1)] = r;
+    }
+  }
+  for (int32_t i = s_nrec + tid; i < nrec; i += NT) {  // the grid covers nrec records: the rest are empty
+    TileRecord r = key_record(-1, 0, 0, 0, 1, 0, 1, -1);
+    work[i] = r;
+  }
+  if (tid == 0) *split_n = s_nsplit;
 }
 
 // ---- one-launch preparation from batched boundaries --------------------------------------
@@ -415,7 +548,7 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
 namespace psb {
 
 hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
-                               int32_t kv_start, int32_t kv_len, int32_t* klo, int32_t* khi, TileRecord* work,
+                               int32_t kv_start, int32_t kv_len, int32_t Hkv, const KeySchedule& ks,
                                hipStream_t stream) {
   const int32_t nkt = (kv_len + kKeyTile - 1) / kKeyTile;
   const int32_t total = B * nkt;
@@ -423,11 +556,11 @@ hipError_t launch_key_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int
   const int waves_per_wg = 256 / kWave;
   const int32_t grid = (total + waves_per_wg - 1) / waves_per_wg;
   key_range_kernel<<<dim3(grid), dim3(256), 0, stream>>>(doc_ids, S, L, seq_start, kv_start, kv_start + kv_len, nkt,
-                                                         total, klo, khi);
+                                                         total, ks.klo, ks.khi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // longest row range first, as for the query side (records with nr = 1: one key tile each)
-  tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(klo, khi, B, nkt, 1, nkt, work);
+  key_plan_kernel<<<dim3(1), dim3(kKeyPlanThreads), 0, stream>>>(ks.klo, ks.khi, B, nkt, Hkv, ks.max_slots, ks.nrec,
+                                                                 ks.tslot, ks.work, ks.split, ks.split_n);
   return hipGetLastError();
 }
 

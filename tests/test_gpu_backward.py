@@ -200,3 +200,26 @@ def test_full_size_one_document(psb, c):
     check_grad(dq[b:b + 1, :, r0:r1].cpu(), rq, f"{lay.name} dq")
     check_grad(dk[b:b + 1, :, d0:d1].cpu(), rk[:, :, d0:d1], f"{lay.name} dk")
     check_grad(dv[b:b + 1, :, d0:d1].cpu(), rv[:, :, d0:d1], f"{lay.name} dv")
+
+
+def test_long_documents_split_key_tiles(psb):
+    # one 4096-token document and a short one: the long document's key tiles see thousands
+    # of rows, so the key-side plan cuts them into row chunks and spends its whole slot
+    # budget (the rest stay whole); gradients still match the oracle and repeat bit for bit
+    S = 4600
+    ids = np.full((1, S), 2, dtype=np.int32)
+    ids[0, :4096] = 1
+    ids[0, 4550:] = oracle.PAD_DOC_ID
+    g = torch.Generator().manual_seed(601)
+    q = torch.randn((1, 4, S, 64), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 2, S, 64), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, 2, S, 64), generator=g).to(torch.bfloat16)
+    grads = run_case(psb, q, k, v, ids, 0, None, True, 602, "bwd split tiles")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    idd = torch.as_tensor(ids).cuda()
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(qd, kd, vd, idd, 0, None, True)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(602)).to(torch.bfloat16).cuda()
+    again = psb.blockdiag_attn_bwd(qd, kd, vd, out, dout, lse, idd, ws, 0, None, True)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b)
