@@ -17,12 +17,15 @@
 //                 forward's plan, recomputes S^T and dP^T = V dO^T (lane = row), and
 //                 accumulates dQ^T += K^T dS^T with the K^T operand gathered from the K
 //                 tile by transposing LDS reads;
-//   dkdv_kernel   key-stationary: a wave owns 32 keys of one kv head (K and V held in
-//                 VGPRs as MFMA B operands), a workgroup 128 keys; it walks every query
-//                 head of the group and the 32-row query tiles that can see its keys,
-//                 recomputes S and dP (lane = key), and accumulates dV^T += dO^T P and
-//                 dK^T += Q^T dS with Q^T / dO^T gathered by transposing LDS reads;
-//                 a step stages 64 rows at D = 128 (two independent 32-row halves).
+//   dkdv_kernel   key-stationary: a wave owns 32 keys of one kv head (K held in VGPRs
+//                 as an MFMA B operand; V too at D = 64, in LDS at D = 128), a workgroup
+//                 128 keys, two waves per SIMD; it walks every query head of the group and
+//                 the query rows that can see its keys, 32 rows per step, recomputes S and
+//                 dP (lane = key), and accumulates dV^T += dO^T P and dK^T += Q^T dS with
+//                 Q^T / dO^T gathered by transposing LDS reads.  When a 128-key tile is
+//                 seen by many rows, the plan splits those rows into chunks that run as
+//                 separate items writing fp32 partial dK / dV, and dkdv_reduce_kernel
+//                 adds each tile's chunks in chunk order.
 // All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the MFMAs that consume them.
 #include <math.h>

@@ -378,10 +378,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
           }
         }
       }
-      float mx = -INFINITY;
+      // row max over the lane's 32 scores as a tree of three-input maxima (v_max3_f32)
+      float m1[11];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(fmaxf(s[0][i], s[0][i + 1]), fmaxf(s[1][i], s[1][i + 1])));
-      return partner_max(mx);
+      for (int j = 0; j < 10; ++j) {
+        const int a = 3 * j, b = 3 * j + 1, c = 3 * j + 2;
+        m1[j] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[c >> 4][c & 15]);
+      }
+      m1[10] = fmaxf(s[1][14], s[1][15]);
+      const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
+      const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+      const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
+      const float m2d = fmaxf(m1[9], m1[10]);
+      return partner_max(fmaxf(fmaxf(fmaxf(m2a, m2b), m2c), m2d));
     };
     // P = exp2(s * sc - m * sc) as bf16 for 16-key step j; l += its row sums
     auto softmax_step = [&](const floatx16 (&s)[2], int j, float nmsc, bf16x8& pj) {
