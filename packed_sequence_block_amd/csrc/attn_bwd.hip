@@ -38,12 +38,11 @@ namespace psb {
 namespace {
 
 constexpr int kBwdWaves = 4;
-// LDS row padding (elements).  Each tile is read both row-wise (ds_read_b128: no bank
-// conflicts for a pitch of 16 bytes mod 32) and through transposing reads (no
-// conflicts for 64 bytes mod 256); no pitch serves both.  Measured: dq keeps the
-// b128-friendly pitch, dk/dv reads Q / dO best at D + 16.
+// LDS row padding (elements) of a tile read only row-wise (ds_read_b128): a pitch of 16
+// bytes mod 256 has no bank conflicts.  A tile also read through transposing reads needs
+// 64 bytes mod 256 there, so no pitch serves both: such tiles (K in dq, Q and dO in dk/dv)
+// are swizzled instead (tile_swz).
 constexpr int DQ_KPAD = 8;
-constexpr int DKV_QPAD = 16;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 constexpr int kKeysPerWave = 32;                       // dkdv: keys per wave
 constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgroup
@@ -92,16 +91,23 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
-  constexpr int KROW = D + DQ_KPAD;                       // padded K / V tile row
-  constexpr int KCH = KROW / 8;                           // 16-byte slots per row
-  constexpr int KSTAGE = kKeysPerTile * KROW;
-  constexpr int KSEGS = kKeysPerTile * KCH / 64;
-  constexpr int KSEG_ITERS = (KSEGS + kBwdWaves - 1) / kBwdWaves;
-  static_assert(KSEGS * 64 == kKeysPerTile * KCH && KSTAGE * 2 == KSEGS * 1024, "tile segments");
+  // K is read row-wise (S^T = K Q^T) and transposed (dQ^T += K^T dS^T): a swizzled tile
+  // of unpadded rows (tile_swz).  V is only read row-wise: rows padded to D + 8.
+  constexpr int KROWB = D * 2;                            // K tile row, bytes
+  constexpr int KSTAGE = kKeysPerTile * D;
+  constexpr int KSEGS = kKeysPerTile * NCH / 64;
+  constexpr int KSEG_ITERS = KSEGS / kBwdWaves;
+  constexpr int VROW = D + DQ_KPAD;                       // padded V tile row
+  constexpr int VCH = VROW / 8;                           // 16-byte slots per row
+  constexpr int VSTAGE = kKeysPerTile * VROW;
+  constexpr int VSEGS = kKeysPerTile * VCH / 64;
+  constexpr int VSEG_ITERS = (VSEGS + kBwdWaves - 1) / kBwdWaves;
+  static_assert(KSEGS % kBwdWaves == 0 && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
+  static_assert(VSEGS * 64 == kKeysPerTile * VCH && VSTAGE * 2 == VSEGS * 1024, "V tile segments");
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV0[KSTAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV1[KSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[VSTAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,16 +117,32 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
   const float sc = p.sc;  // |scale| * log2(e); Q is sign-flipped for a negative scale
   const floatx16 zero16 = {};
 
+  // slot seg * 64 + lane of a K tile holds row slot / NCH, stored chunk slot % NCH, which is
+  // global chunk (stored chunk) ^ tile_swz(row); V slots are row-major with pad slots
   int32_t koff[KSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < KSEG_ITERS; ++j) {
     const int slot = (j * kBwdWaves + wv) * 64 + lane;
-    const int row = slot / KCH, ch = slot % KCH;
-    koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+    const int row = slot / NCH, pc = slot % NCH;
+    koff[j] = row * row_bytes + 16 * (pc ^ tile_swz<D>(row));
   }
-  const int k_rd = lr * KROW + 8 * h;  // row-major operand read base (A = K or V rows)
-  // transposing read of K^T: key (16 j + 4 h + (lane & 15) / 4) [+ 8], d (32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3))
-  const int kt_rd = (4 * h + ((lane & 15) >> 2)) * KROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int32_t voff[VSEG_ITERS];
+#pragma unroll
+  for (int j = 0; j < VSEG_ITERS; ++j) {
+    const int slot = (j * kBwdWaves + wv) * 64 + lane;
+    const int row = slot / VCH, ch = slot % VCH;
+    voff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+  }
+  // A = K rows, byte address: k-step ks reads chunk 2 ks + h of row lr, stored at
+  // k_rd ^ (32 ks) (the chunk bits and the row bits never overlap)
+  const int k_rd = lr * KROWB + 16 * (h ^ tile_swz<D>(lr));
+  const int v_rd = lr * VROW + 8 * h;  // A = V rows, element index
+  // transposing read of K^T: key r0 = 4 h + (lane & 15) / 4 (+ 16 j + 32 kb, + 8 for the
+  // pair's second read), d bytes 64 db + 32 ((lane >> 4) & 1) + 8 (lane & 3); stored at
+  // kt_rd ^ (64 db) (second read: ^ 32, 8 rows on)
+  const int kt_r0 = 4 * h + ((lane & 15) >> 2);
+  const int kt_rd = kt_r0 * KROWB + 16 * ((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ tile_swz<D>(kt_r0)) +
+                    8 * (lane & 1);
 
   for (int64_t item = blockIdx.x; item < p.items; item += gridDim.x) {
     const int32_t rank = (int32_t)(item / p.units), unit = (int32_t)(item % p.units);
@@ -153,13 +175,21 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
     const __bf16* kbase = p.k + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
     const __bf16* vbase = p.v + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
-    auto issue = [&](const __bf16* base, __bf16* buf, int32_t kt) {
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(base + (int64_t)(kt - p.kv_start) * D), (short)0, min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+    auto rsrc = [&](const __bf16* base, int32_t kt) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)(kt - p.kv_start) * D), (short)0,
+                                               min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+    };
+    auto issue_k = [&](__bf16* buf, int32_t kt) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(kbase, kt);
 #pragma unroll
-      for (int j = 0; j < KSEG_ITERS; ++j) {
+      for (int j = 0; j < KSEG_ITERS; ++j) buffer_load_lds16(r, buf + (j * kBwdWaves + wv) * 512, koff[j]);
+    };
+    auto issue_v = [&](__bf16* buf, int32_t kt) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(vbase, kt);
+#pragma unroll
+      for (int j = 0; j < VSEG_ITERS; ++j) {
         const int seg = j * kBwdWaves + wv;
-        if (KSEGS % kBwdWaves == 0 || seg < KSEGS) buffer_load_lds16(r, buf + seg * 512, koff[j]);
+        if (VSEGS % kBwdWaves == 0 || seg < VSEGS) buffer_load_lds16(r, buf + seg * 512, voff[j]);
       }
     };
 
@@ -229,11 +259,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     auto half = [&](const __bf16* kbuf, const __bf16* vbuf, int32_t kt, int kb) {
       // S^T and dP^T for keys 32 kb .. 32 kb + 31
       floatx16 s = zero16, dp = zero16;
-      const __bf16* kp = kbuf + k_rd + 32 * KROW * kb;
-      const __bf16* vp = vbuf + k_rd + 32 * KROW * kb;
+      const char* kp = (const char*)kbuf + 32 * KROWB * kb;
+      const __bf16* vp = vbuf + v_rd + 32 * VROW * kb;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(kp + 16 * ks);
+        const bf16x8 a = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
         const bf16x8 c = *(const bf16x8*)(vp + 16 * ks);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, oreg[ks], dp, 0, 0, 0);
@@ -262,25 +292,25 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       // dQ^T += K^T dS^T over the two 16-key steps of this half
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const __bf16* tp = kbuf + kt_rd + (32 * kb + 16 * j) * KROW;
+        const char* tp = (const char*)kbuf + (32 * kb + 16 * j) * KROWB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = vtr_pair(tp + 32 * db, 8 * KROW);
+          const bf16x8 a = vtr_pair_at(tp + (kt_rd ^ (64 * db)), tp + 8 * KROWB + (kt_rd ^ (64 * db + 32)));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsk[j], acc[db], 0, 0, 0);
         }
       }
     };
 
     __syncthreads();  // the previous item no longer reads LDS
-    issue(kbase, sK0, tlo);
-    issue(vbase, sV0, tlo);
+    issue_k(sK0, tlo);
+    issue_v(sV0, tlo);
     auto step = [&](int32_t t, const __bf16* kc, __bf16* kn, const __bf16* vc, __bf16* vn) {
       const int32_t kt = tlo + t * kKeysPerTile;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (t + 1 < ntiles) {
-        issue(kbase, kn, kt + kKeysPerTile);
-        issue(vbase, vn, kt + kKeysPerTile);
+        issue_k(kn, kt + kKeysPerTile);
+        issue_v(vn, kt + kKeysPerTile);
       }
       half(kc, vc, kt, 0);
       half(kc, vc, kt, 1);
@@ -314,12 +344,14 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
-  constexpr int QROW = D + DKV_QPAD;                          // padded Q / dO tile row
-  constexpr int QCH = QROW / 8;                               // 16-byte slots per row
-  constexpr int QSLOTS = kRowsPerStep * QCH;                  // 16-byte slots of a tile
-  constexpr int QSEGS = (QSLOTS + 63) / 64;                   // 1 KiB wave-wide loads
+  // Q and dO tiles are read row-wise (S = Q K^T, dP = dO V^T) and transposed (dK^T +=
+  // Q^T dS, dV^T += dO^T P): swizzled tiles of unpadded rows (tile_swz)
+  constexpr int QROWB = D * 2;                                // Q / dO tile row, bytes
+  constexpr int QSLOTS = kRowsPerStep * NCH;                  // 16-byte slots of a tile
+  constexpr int QSEGS = QSLOTS / 64;                          // 1 KiB wave-wide loads
   constexpr int QSEG_ITERS = (QSEGS + kBwdWaves - 1) / kBwdWaves;
-  constexpr int QSTAGE = QSEGS * 512;                         // elements (last segment partly spare)
+  constexpr int QSTAGE = QSEGS * 512;                         // elements
+  static_assert(QSEGS * 64 == QSLOTS, "Q tile segments");
   __shared__ __attribute__((aligned(1024))) __bf16 sQ0[QSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sQ1[QSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sO0[QSTAGE];
@@ -338,16 +370,23 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
   const int32_t nkt = p.nkt;
   static_assert(kKeysPerItem == kKeyTile, "key tiles of the plan");
 
+  // slot seg * 64 + lane holds row slot / NCH, stored chunk slot % NCH = global chunk ^
+  // tile_swz(row)
   int32_t qoff[QSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < QSEG_ITERS; ++j) {
     const int slot = (j * kBwdWaves + wv) * 64 + lane;
-    const int row = slot / QCH, ch = slot % QCH;
-    qoff[j] = (slot < QSLOTS && ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+    const int row = slot / NCH, pc = slot % NCH;
+    qoff[j] = (slot < QSLOTS) ? row * row_bytes + 16 * (pc ^ tile_swz<D>(row)) : 0x7ffffff0;
   }
-  const int a_rd = lr * QROW + 8 * h;  // A = Q / dO rows (lane = row)
-  // transposing read of Q^T / dO^T: row (16 j + 4 h + (lane & 15) / 4) [+ 8], d (32 db + ...)
-  const int t_rd = (4 * h + ((lane & 15) >> 2)) * QROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // A = Q / dO rows (lane = row), bytes: k-step ks reads chunk 2 ks + h of row lr at a_rd ^ (32 ks)
+  const int a_rd = lr * QROWB + 16 * (h ^ tile_swz<D>(lr));
+  // transposing read of Q^T / dO^T: row r0 = 4 h + (lane & 15) / 4 (+ 16 j, + 8 for the pair's
+  // second read), d bytes 64 db + 32 ((lane >> 4) & 1) + 8 (lane & 3): at t_rd ^ (64 db), the
+  // second read at t_rd ^ (64 db + 32) 8 rows on
+  const int t_r0 = 4 * h + ((lane & 15) >> 2);
+  const int t_rd = t_r0 * QROWB + 16 * ((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ tile_swz<D>(t_r0)) +
+                   8 * (lane & 1);
 
   // item = key-tile rank x kv head; kv head = item % Hkv keeps (with 8 kv heads) one kv
   // head per XCD
@@ -531,8 +570,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int hf = 0; hf < NHALF; ++hf) {
-          const bf16x8 aq = *(const bf16x8*)(qb + a_rd + 32 * hf * QROW + 16 * ks);
-          const bf16x8 ao = *(const bf16x8*)(ob + a_rd + 32 * hf * QROW + 16 * ks);
+          const bf16x8 aq = *(const bf16x8*)((const char*)qb + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
+          const bf16x8 ao = *(const bf16x8*)((const char*)ob + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
           s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
           const bf16x8 bv = VLDS ? *(const bf16x8*)(sV + v_rd + 16 * ks) : vreg[ks];
           dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, dp[hf], 0, 0, 0);
@@ -584,12 +623,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
       for (int hf = 0; hf < NHALF; ++hf) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const __bf16* to = ob + t_rd + (32 * hf + 16 * j) * QROW;
-          const __bf16* tq = qb + t_rd + (32 * hf + 16 * j) * QROW;
+          const char* to = (const char*)ob + (32 * hf + 16 * j) * QROWB;
+          const char* tq = (const char*)qb + (32 * hf + 16 * j) * QROWB;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 ao = vtr_pair(to + 32 * db, 8 * QROW);
-            const bf16x8 aq = vtr_pair(tq + 32 * db, 8 * QROW);
+            const int t0 = t_rd ^ (64 * db), t1 = 8 * QROWB + (t_rd ^ (64 * db + 32));
+            const bf16x8 ao = vtr_pair_at(to + t0, to + t1);
+            const bf16x8 aq = vtr_pair_at(tq + t0, tq + t1);
             dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pk[hf][j], dva[db], 0, 0, 0);
             dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsk[hf][j], dka[db], 0, 0, 0);
           }

@@ -36,6 +36,30 @@ __device__ __forceinline__ bf16x8 vtr_pair(const __bf16* p, int row8) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// the same pair from two byte addresses (swizzled tiles, where the second read's chunk
+// differs from the first's)
+__device__ __forceinline__ bf16x8 vtr_pair_at(const char* p0, const char* p1) {
+  const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p0));
+  const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Swizzled LDS tile for a tile read both row-wise (ds_read_b128: 16 lanes, 16 rows, one
+// 16-byte chunk each) and through transposing reads (ds_read_b64_tr_b16: 32 lanes, 4
+// aligned rows, 64 bytes = 4 chunks each).  Rows hold D elements with no padding and
+// chunk c of row r sits at chunk c ^ tile_swz(r).  Assuming 64 four-byte banks, the
+// row-wise read needs tile_swz to be one-to-one over 16 consecutive rows within each
+// 256-byte bank window; the transposing read needs the 4 rows' chunk quads (c / 4) ^
+// (tile_swz(r) / 4) to differ within a window.  D = 128 (one row per window):
+// 4 (r % 4) + (r / 4) % 4; D = 64 (two rows per window, told apart by r % 2):
+// 4 ((r / 2) % 2) + (r / 4) % 4.  Rows 8 apart differ only in bit 1 of tile_swz, so
+// the second read of a transposing pair is the first's address ^ 32 plus 8 rows.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  static_assert(D == 64 || D == 128, "head dims");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
 __device__ __forceinline__ bf16x2 cvt_bf16x2(float a, float b) {
   const float2v f = {a, b};
   return __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
