@@ -71,16 +71,23 @@ struct AttnParams {
 // it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
 constexpr float kRescaleLog2 = 8.0f;
 
-// LDS tiles, row-major, 64 keys each; every address is a per-lane base plus a
-// compile-time offset.
-//   K: rows of D + 8 bf16.  The 16-byte padding puts the 16 rows that one b128 read
-//      touches per cycle on distinct bank groups.
-//   V: rows of D + 32 bf16.  A PV k-step feeds lane (h = lane / 32) the keys
-//      16j + 4h + {0..3} and 16j + 8 + 4h + {0..3} of one d: two ds_read_b64_tr_b16,
-//      each gathering 4 keys x 4 d from 16 lanes' row addresses and handing every lane
-//      its own d.  One half-wave of such a read covers 4 rows x 64 bytes; a row pitch
-//      of 64 bytes mod 256 puts those on distinct banks (D + 8 or D + 16 leaves 2- to
-//      4-way conflicts).
+// LDS tiles, 64 keys each, rows of D bf16 with no padding; 16-byte chunk c of row r is
+// stored at chunk c ^ f(r), so that every read is free of bank conflicts (64 banks of 4
+// bytes) and a load fills whole 1 KiB segments with data:
+//   K: f = tile_swz (one-to-one over 16 consecutive rows): the 16 rows that one b128 read
+//      serves per pass land on distinct bank groups.  The read of k-step ks sits at the
+//      lane's base ^ (32 ks).
+//   V: a PV k-step feeds lane (h = lane / 32) the keys 16j + 4h + {0..3} and
+//      16j + 8 + 4h + {0..3} of one d: two ds_read_b64_tr_b16, each gathering 4 keys x 4 d
+//      from 16 lanes' row addresses and handing every lane its own d.  One half-wave of
+//      such a read covers 4 aligned rows x 64 bytes (a chunk quad); f = 4 (r % 4) at
+//      D = 128 (one row per 256-byte bank window) or 4 ((r / 2) % 2) at D = 64 (two rows
+//      per window) puts the 4 rows' quads on distinct banks.  Rows 8 apart share f, so
+//      both reads of a pair use the lane's base ^ (64 db).
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // DENSE: the explicit-mask variant (the dense-mask path next to the varlen kernels in
 // the blockdiag_cp package overview).  No plan: every row tile walks all keys [0, S) and
@@ -90,18 +97,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   constexpr int NR = kWaves / NH;
   constexpr int KS = D / 16;                              // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;                              // 32-row blocks of O^T
-  constexpr int NCH = D / 8;                              // 16-byte chunks per K row
-  constexpr int KROW = D + 8;                             // padded K row, elements
-  constexpr int VROW = D + 32;                            // padded V row, elements
-  constexpr int KSTAGE = kKeysPerTile * KROW;             // elements per K stage
-  constexpr int VSTAGE = kKeysPerTile * VROW;             // elements per V stage
-  constexpr int VNCH = VROW / 8;                          // 16-byte slots per V row
-  constexpr int VSEGS = kKeysPerTile * VNCH / 64;
+  constexpr int NCH = D / 8;                              // 16-byte chunks per K / V row
+  constexpr int ROWB = D * 2;                             // K / V tile row, bytes
+  constexpr int KSTAGE = kKeysPerTile * D;                // elements per K stage
+  constexpr int VSTAGE = kKeysPerTile * D;                // elements per V stage
+  constexpr int VSEGS = kKeysPerTile * NCH / 64;          // 1 KiB wave-wide loads per V tile
   constexpr int VSEG_ITERS = (VSEGS + kWaves - 1) / kWaves;
-  static_assert(VSEGS * 64 == kKeysPerTile * VNCH && VSTAGE * 2 == VSEGS * 1024, "V tile segments");
-  constexpr int KSEGS = kKeysPerTile * (NCH + 1) / 64;    // 1 KiB wave-wide loads per K tile
+  static_assert(VSEGS * 64 == kKeysPerTile * NCH && VSTAGE * 2 == VSEGS * 1024, "V tile segments");
+  constexpr int KSEGS = kKeysPerTile * NCH / 64;          // 1 KiB wave-wide loads per K tile
   constexpr int KSEG_ITERS = (KSEGS + kWaves - 1) / kWaves;
-  static_assert(KSEGS * 64 == kKeysPerTile * (NCH + 1) && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
+  static_assert(KSEGS * 64 == kKeysPerTile * NCH && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
 
   // Two K and two V stages as separate objects, so the compiler can tell a load in
   // flight into one from reads of the other (the tile loop is unrolled by two for that
@@ -126,25 +131,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
 
   // K and V loads: lane `lane` of segment seg fills 16-byte slot seg*64 + lane of the
-  // padded tile; slot -> (row, chunk); pad slots get an offset past every buffer, so the
-  // load returns 0 and the padding holds zeros
+  // tile, i.e. row slot / NCH at stored chunk slot % NCH, which holds global chunk
+  // (stored chunk) ^ f(row)
   int32_t koff[KSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < KSEG_ITERS; ++j) {
     const int slot = (j * kWaves + wv) * 64 + lane;
-    const int row = slot / (NCH + 1), ch = slot % (NCH + 1);
-    koff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+    const int row = slot / NCH, pc = slot % NCH;
+    koff[j] = row * row_bytes + 16 * (pc ^ tile_swz<D>(row));
   }
   int32_t voff[VSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < VSEG_ITERS; ++j) {
     const int slot = (j * kWaves + wv) * 64 + lane;
-    const int row = slot / VNCH, ch = slot % VNCH;
-    voff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
+    const int row = slot / NCH, pc = slot % NCH;
+    voff[j] = row * row_bytes + 16 * (pc ^ v_swz<D>(row));
   }
-  const int k_rd = lr * KROW + 8 * h;                    // K operand read base (element)
-  // tr read: lane reads 4 d at row (16 j + 4 h + (lane & 15) / 4) [+ 8], col 32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3)
-  const int vt_rd = (4 * h + ((lane & 15) >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // K operand (rows lr and lr + 32, chunk 2 ks + h), byte address: k_rd ^ (32 ks)
+  const int k_rd = lr * ROWB + 16 * (h ^ tile_swz<D>(lr));
+  // tr read: lane reads 4 d at row r0 = 4 h + (lane & 15) / 4 (+ 16 j, + 8), d bytes
+  // 64 db + 32 ((lane >> 4) & 1) + 8 (lane & 3): byte address vt_rd ^ (64 db)
+  const int vt_r0 = 4 * h + ((lane & 15) >> 2);
+  const int vt_rd = vt_r0 * ROWB + 16 * ((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ v_swz<D>(vt_r0)) +
+                    8 * (lane & 1);
 
   // workgroup blockIdx.x takes items blockIdx.x, + gridDim.x, ... (one item when the
   // grid covers them all); with 8 kv heads, unit % Hkv == blockIdx.x % 8 keeps each
@@ -300,20 +309,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
                   __amdgpu_buffer_rsrc_t rvn, __bf16* vnext) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
-      const __bf16* kp = kbuf + k_rd;
+      const char* kp = (const char*)kbuf;
       constexpr int AH = (KS < 2) ? KS : 2;
       bf16x8 ka[AH][2];
 #pragma unroll
       for (int ks = 0; ks < AH; ++ks) {
-        ka[ks][0] = *(const bf16x8*)(kp + 16 * ks);
-        ka[ks][1] = *(const bf16x8*)(kp + 32 * KROW + 16 * ks);
+        ka[ks][0] = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
+        ka[ks][1] = *(const bf16x8*)(kp + 32 * ROWB + (k_rd ^ (32 * ks)));
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a0 = ka[ks % AH][0], a1 = ka[ks % AH][1];
         if (ks + AH < KS) {
-          ka[ks % AH][0] = *(const bf16x8*)(kp + 16 * (ks + AH));
-          ka[ks % AH][1] = *(const bf16x8*)(kp + 32 * KROW + 16 * (ks + AH));
+          ka[ks % AH][0] = *(const bf16x8*)(kp + (k_rd ^ (32 * (ks + AH))));
+          ka[ks % AH][1] = *(const bf16x8*)(kp + 32 * ROWB + (k_rd ^ (32 * (ks + AH))));
         }
         s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], ks ? s[0] : zero16, 0, 0, 0);
         s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], ks ? s[1] : zero16, 0, 0, 0);
@@ -409,14 +418,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // softmax(t) fused with PV(t): P for 16-key step j is produced while the MFMAs of
     // step j-1 run (about 6 VALU ops per MFMA); V^T operands are read one step ahead.
     // A hard scheduling barrier between steps keeps the interleaving.
-    auto vtr = [&](const __bf16* ptr) { return vtr_pair(ptr, 8 * VROW); };
+    // V^T operand of 16-key step j, d block db: rows 16 j + ... and 8 rows on, same chunks
+    auto vtr = [&](const char* vb, int j, int db) {
+      const char* a = vb + 16 * j * ROWB + (vt_rd ^ (64 * db));
+      return vtr_pair_at(a, a + 8 * ROWB);
+    };
     auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf) {
       const float nmsc = nmscale();
-      const __bf16* vp = vbuf + vt_rd;
+      const char* vb = (const char*)vbuf;
       bf16x8 pk[4];
       bf16x8 va[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[db] = vtr(vp + 32 * db);
+      for (int db = 0; db < DB; ++db) va[db] = vtr(vb, 0, db);
       softmax_step(s, 0, nmsc, pk[0]);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
@@ -425,7 +438,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk[j], o[db], 0, 0, 0);
-          if (j < 3) va[db] = vtr(vp + 32 * db + 16 * (j + 1) * VROW);
+          if (j < 3) va[db] = vtr(vb, j + 1, db);
         }
         if (j < 3) {
           softmax_step(s, j + 1, nmsc, pk[j + 1]);
