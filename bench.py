@@ -20,9 +20,11 @@ same steps and never exceeds `ms_per_step`.  `sub_configs` repeats the same
 measurement for workloads 2-4 (five repeats of enough steps to last >= 100 ms,
 median reported).  `traffic` is HBM bytes per launch from the committed
 rocprofv3 counter runs, reported only while the kernel source is unchanged;
-`backward` times the training path's backward (dq, dk, dv); `cpu_baseline`
-times the CPU fp64 oracle on the host cores over a bounded sample of the
-headline workload.
+`backward` times the training path's backward (dq, dk, dv).  Every other timed
+quantity (backward, preparation, boundary variants, key window, dense mask,
+drop-in) is the median of five repeats of back-to-back calls lasting >= 100 ms
+each.  `cpu_baseline` times the CPU fp64 oracle on the host cores over a bounded
+sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -264,11 +266,17 @@ def dropin_leg(psb, lay, q, k, v, doc_ids, steps):
         for _ in range(3):  # the first backward also starts autograd's device thread
             fn()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        res[name] = round((time.perf_counter() - t0) * 1e3 / n, 5)
+
+        def burst(m):
+            t0 = time.perf_counter()
+            for _ in range(m):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / m
+
+        est = burst(n)
+        m = max(n, int(100.0 / max(est, 1e-3)) + 1)
+        res[name] = round(statistics.median(burst(m) for _ in range(5)), 5)
     res["what"] = "F.scaled_dot_product_attention swapped for the packed path (custom ops), wall clock"
     return res
 
@@ -330,15 +338,23 @@ class Problem:
         self.prepare, self.boundary, self.plan, self.attention = prepare, boundary, plan, attention
 
     def timed(self, fn, n):
-        """n back-to-back calls between one pair of events on the launch stream (ms per call)."""
+        """ms per call: back-to-back calls between one pair of events on the launch stream,
+        at least n of them and enough to last >= 100 ms (a short burst after an idle
+        device runs at a lower clock), repeated five times; the median of the repeats."""
         import torch
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(self.stream)
-        for _ in range(n):
-            fn()
-        a1.record(self.stream)
-        torch.cuda.synchronize()
-        return a0.elapsed_time(a1) / n
+
+        def burst(m):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(self.stream)
+            for _ in range(m):
+                fn()
+            a1.record(self.stream)
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / m
+
+        est = burst(max(1, n))
+        m = max(n, int(100.0 / max(est, 1e-3)) + 1)
+        return statistics.median(burst(m) for _ in range(5))
 
     def time_steps(self, n):
         """n steps between two device synchronizations, wall clock; an event pair on the
