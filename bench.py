@@ -12,7 +12,9 @@ The metric is useful TFLOP/s = 4 * D * Hq * allowed_pairs / step time.
 
 Headline workload (default --config 5): the long mixed row (B=1, S=L=65536,
 Hq=64, Hkv=4, D=64, 80% uniform[64, 1024] / 20% uniform[8192, 24576] document
-lengths, seed 5), the largest of the five workloads.  Exactly K steps are timed
+lengths, seed 5), the largest of the five workloads.  About 150 ms of untimed
+steps warm the device up (its clock ramps under load), then W warmup steps run
+and exactly K steps are timed
 by the wall clock between two device synchronizations; inside that window an
 event pair on the launch stream brackets every attention launch, so
 `roofline.kernel_ms` (the mean of those launch durations) is measured over the
@@ -451,6 +453,12 @@ def main():
     lay = pb.lay
     B, Hq, Hkv, L, S, D = lay.B, lay.Hq, lay.Hkv, lay.L, lay.S, lay.D
 
+    # device warm-up, untimed: the clock ramps up over the first ~100 ms of load, so a
+    # workload whose timed steps last only a few ms would otherwise be measured cold
+    est, _, _ = pb.time_steps(2)
+    for _ in range(max(1, int(150.0 / max(est, 1e-3)))):
+        pb.prepare()
+        pb.attention()
     for _ in range(args.warmup):
         pb.prepare()
         pb.attention()

@@ -35,7 +35,8 @@ def run_case(psb, lay, seed_base=None, scale=None, ids=None):
 
 
 def test_config1_full(psb):
-    run_case(psb, make_layout(1))
+    mx, mean = run_case(psb, make_layout(1))
+    say("config 1 whole output max/mean abs err", mx, mean)
 
 
 SMALL = [
