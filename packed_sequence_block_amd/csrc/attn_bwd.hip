@@ -30,6 +30,8 @@
 // rounded to bf16 for the MFMAs that consume them.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "psb_internal.h"
 #include "schedule.h"
@@ -271,24 +273,37 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
       const int32_t e = kt + 32 * kb + 4 * h - kshift;
       bf16x8 dsk[2];
+      // dS = P * (dP - delta) rounded to bf16; a tile inside one document's causal triangle
+      // for every row of the wave takes the copy without the per-key range test (the
+      // condition is wave-uniform, so the branch costs nothing and saves three VALU ops
+      // per score)
+      auto ds_step = [&](auto masked) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float d2[2];
+          for (int t = 0; t < 8; t += 2) {
+            float d2[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 8 * j + t + u;
-            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
-            const bool ok = full || rel <= span;
-            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -lse2)) : 0.f;
-            d2[u] = pr * (dp[i] - dlt);
+            for (int u = 0; u < 2; ++u) {
+              const int i = 8 * j + t + u;
+              const float arg = __builtin_fmaf(s[i], sc, -lse2);
+              float pr;
+              if constexpr (decltype(masked)::value) {
+                const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
+                pr = (rel <= span) ? __builtin_amdgcn_exp2f(arg) : 0.f;
+              } else {
+                pr = __builtin_amdgcn_exp2f(arg);
+              }
+              d2[u] = pr * (dp[i] - dlt);
+            }
+            const bf16x2 pk = cvt_bf16x2(d2[0], d2[1]);
+            dsk[j][t] = pk[0];
+            dsk[j][t + 1] = pk[1];
           }
-          const bf16x2 pk = cvt_bf16x2(d2[0], d2[1]);
-          dsk[j][t] = pk[0];
-          dsk[j][t + 1] = pk[1];
         }
-      }
+      };
+      if (full) ds_step(std::false_type{});
+      else ds_step(std::true_type{});
       // dQ^T += K^T dS^T over the two 16-key steps of this half
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -451,6 +466,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
     }
     if (r_hi < r_lo) r_hi = r_lo;
     // wave range: min / max over its keys (empty keys excluded)
+    // and the rows every key of the wave sees: [max r_lo, min r_hi) (empty when some key
+    // sees no row), so that a step inside it needs no per-row test
+    // (only used at D = 64: at D = 128 the unmasked copy below would push the kernel past
+    // its 256 registers)
+    int32_t full_lo = 0x7fffffff, full_hi = 0;
     {
       int32_t lo_m = (r_hi > r_lo) ? r_lo : 0x7fffffff, hi_m = (r_hi > r_lo) ? r_hi : 0;
 #pragma unroll
@@ -459,6 +479,16 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
         hi_m = max(hi_m, __shfl_xor(hi_m, off, kWave));
       }
       if (lane == 0) { s_rng[wv][0] = lo_m; s_rng[wv][1] = hi_m; }
+      if constexpr (D == 64) {
+        int32_t lo_x = (r_hi > r_lo) ? r_lo : 0x7fffffff, hi_n = (r_hi > r_lo) ? r_hi : 0;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          lo_x = max(lo_x, __shfl_xor(lo_x, off, kWave));
+          hi_n = min(hi_n, __shfl_xor(hi_n, off, kWave));
+        }
+        full_lo = __builtin_amdgcn_readfirstlane(lo_x);
+        full_hi = __builtin_amdgcn_readfirstlane(hi_n);
+      }
     }
     __syncthreads();
     int32_t wg_lo = 0x7fffffff, wg_hi = 0;
@@ -589,32 +619,76 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
         for (int j = KS; j < QFULL; ++j) issue_seg(rn, qn, on, j);
       }
       bf16x8 pk[NHALF][2], dsk[NHALF][2];
+      // P and dS; a step whose rows all see every key of the wave takes the copy without the
+      // per-row test (wave-uniform condition)
+      auto p_ds = [&](auto masked) {
 #pragma unroll
-      for (int hf = 0; hf < NHALF; ++hf) {
+        for (int hf = 0; hf < NHALF; ++hf) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float4 l4 = *(const float4*)&sL[stage][32 * hf + 8 * a + 4 * h];
-          const float4 d4 = *(const float4*)&sDl[stage][32 * hf + 8 * a + 4 * h];
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          for (int a = 0; a < 4; ++a) {
+            const float4 l4 = *(const float4*)&sL[stage][32 * hf + 8 * a + 4 * h];
+            const float4 d4 = *(const float4*)&sDl[stage][32 * hf + 8 * a + 4 * h];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-          for (int c = 0; c < 4; c += 2) {
-            float pp[2], dd[2];
+            for (int c = 0; c < 4; c += 2) {
+              float pp[2], dd[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int i = 4 * a + c + u;
-              const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
-              const bool ok = (uint32_t)(r - r_lo) < kspan;
-              const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
-              const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
-              pp[u] = pr;
-              dd[u] = pr * (dp[hf][i] - dv4[c + u]);
+              for (int u = 0; u < 2; ++u) {
+                const int i = 4 * a + c + u;
+                const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
+                float pr;
+                if constexpr (decltype(masked)::value) {
+                  const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
+                  pr = ((uint32_t)(r - r_lo) < kspan) ? __builtin_amdgcn_exp2f(arg) : 0.f;
+                } else {
+                  pr = __builtin_amdgcn_exp2f(arg);
+                }
+                pp[u] = pr;
+                dd[u] = pr * (dp[hf][i] - dv4[c + u]);
+              }
+              const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
+              const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
+              const int j = a >> 1, t = 4 * (a & 1) + c;
+              pk[hf][j][t] = p2[0]; pk[hf][j][t + 1] = p2[1];
+              dsk[hf][j][t] = d2[0]; dsk[hf][j][t + 1] = d2[1];
             }
-            const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
-            const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
-            const int j = a >> 1, t = 4 * (a & 1) + c;
-            pk[hf][j][t] = p2[0]; pk[hf][j][t + 1] = p2[1];
-            dsk[hf][j][t] = d2[0]; dsk[hf][j][t + 1] = d2[1];
+          }
+        }
+      };
+      if constexpr (D == 64) {
+        if (rr >= full_lo && rr + kRowsPerStep <= full_hi) p_ds(std::false_type{});
+        else p_ds(std::true_type{});
+      } else {
+        // the masked loop written out: at D = 128 the same loop through p_ds (one copy only)
+        // compiled to 26 spilled registers instead of 10
+#pragma unroll
+        for (int hf = 0; hf < NHALF; ++hf) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float4 l4 = *(const float4*)&sL[stage][32 * hf + 8 * a + 4 * h];
+            const float4 d4 = *(const float4*)&sDl[stage][32 * hf + 8 * a + 4 * h];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int c = 0; c < 4; c += 2) {
+              float pp[2], dd[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int i = 4 * a + c + u;
+                const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
+                const bool ok = (uint32_t)(r - r_lo) < kspan;
+                const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
+                const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
+                pp[u] = pr;
+                dd[u] = pr * (dp[hf][i] - dv4[c + u]);
+              }
+              const bf16x2 p2 = cvt_bf16x2(pp[0], pp[1]);
+              const bf16x2 d2 = cvt_bf16x2(dd[0], dd[1]);
+              const int j = a >> 1, t = 4 * (a & 1) + c;
+              pk[hf][j][t] = p2[0]; pk[hf][j][t + 1] = p2[1];
+              dsk[hf][j][t] = d2[0]; dsk[hf][j][t + 1] = d2[1];
+            }
           }
         }
       }
