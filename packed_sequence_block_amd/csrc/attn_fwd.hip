@@ -297,7 +297,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     floatx16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16;
-    float m_run = -INFINITY, l_run = 0.f;
+    // running max m (raw score units), the exp2 offset -m sc and the rescale threshold
+    // m + 2^8 / sc; all start at "no key yet" (-inf, 0, -inf)
+    float m_run = -INFINITY, l_run = 0.f, nmsc = 0.f, m_thr = -INFINITY;
+    const float thr_gap = kRescaleLog2 / sc;
 
     // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
     // operands read two k-steps ahead of their MFMAs
@@ -414,7 +417,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       pj = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto nmscale = [&]() { return (m_run == -INFINITY) ? 0.f : -m_run * sc; };
     // softmax(t) fused with PV(t): P for 16-key step j is produced while the MFMAs of
     // step j-1 run (about 6 VALU ops per MFMA); V^T operands are read one step ahead.
     // A hard scheduling barrier between steps keeps the interleaving.
@@ -424,7 +426,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       return vtr_pair_at(a, a + 8 * ROWB);
     };
     auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf) {
-      const float nmsc = nmscale();
       const char* vb = (const char*)vbuf;
       bf16x8 pk[4];
       bf16x8 va[DB];
@@ -454,14 +455,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_s_setprio(0);
     };
     // lazy running max: m moves (and O, l are rescaled) only when the tile max exceeds
-    // it by more than 2^8 in the exp2 domain
-    auto grows = [&](float mx, float& m_cand) {
-      m_cand = fmaxf(m_run, mx);
-      return (m_cand != -INFINITY) && (m_run == -INFINITY || (m_cand - m_run) * sc > kRescaleLog2);
-    };
-    auto rescale = [&](bool grow, float m_cand) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_cand) * sc) : 1.f;
-      m_run = grow ? m_cand : m_run;
+    // it by more than 2^8 in the exp2 domain, i.e. exceeds m_thr (-inf until the first
+    // key, so the first finite score always moves it; alpha is then exp2(-inf) = 0 on an
+    // O and l that are still 0)
+    auto rescale = [&](float mx) {
+      const bool grow = mx > m_thr;
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * sc) : 1.f;
+      m_run = grow ? mx : m_run;
+      m_thr = grow ? mx + thr_gap : m_thr;
+      nmsc = grow ? -mx * sc : nmsc;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -493,9 +495,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       qk(kcur, st_s, rkn, knext, rvn, vnext);
       if (more) load_mask(kt + kKeysPerTile, mnext);
       apply_mask(st_s, mcur);
-      float m_cand;
-      const bool g = grows(mask_max(kt, st_s), m_cand);
-      if (__builtin_amdgcn_readfirstlane(__ballot(g) != 0)) rescale(g, m_cand);
+      const float mx = mask_max(kt, st_s);
+      if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) rescale(mx);  // wave-uniform (scalar) test
       softmax_pv(st_s, vcur);
     };
     int32_t t = 0;

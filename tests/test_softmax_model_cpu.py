@@ -4,8 +4,9 @@ The forward kernel walks 64-key tiles and keeps, per query row, a running maximu
 of the raw scores, a running sum l and an fp32 accumulator o (online softmax in the
 exp2 domain with sc = |scale| * log2(e)):
   * masked scores become -inf; the tile maximum is taken over raw scores;
-  * m moves only when the tile maximum exceeds it by more than 2^8 in the exp2
-    domain (or m is still -inf); l and o are then multiplied by exp2((m - m') sc);
+  * m moves only when the tile maximum exceeds the threshold m + 2^8 / sc (float32,
+    -inf until the first key); then m' = tile maximum and l, o are multiplied by
+    exp2((m - m') sc);
   * p = exp2(s sc - m sc) (one fused multiply-add), rounded to bf16; l adds the bf16
     p, o adds p times v;
   * the output is o / l (0 when l == 0), rounded to bf16.
@@ -46,16 +47,19 @@ def model_row(qrow, keys, vals, allowed, scale, clamp=True):
     q = -qrow if np.signbit(np.float32(scale)) and scale != 0 else qrow
     s_all = (keys.astype(np.float32) @ q.astype(np.float32)).astype(np.float32)
     m = np.float32(-np.inf)
+    m_thr = np.float32(-np.inf)
+    with np.errstate(over="ignore", divide="ignore"):  # 2^8 / sc is +inf at sc = FLT_MIN, as in float32 on the GPU
+        gap = np.float32(np.float32(RESCALE_LOG2) / sc)
     l = np.float32(0.0)
     o = np.zeros(vals.shape[1], dtype=np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         for t0 in range(0, keys.shape[0], TILE):
             s = np.where(allowed[t0:t0 + TILE], s_all[t0:t0 + TILE], np.float32(-np.inf)).astype(np.float32)
             mx = np.float32(s.max())
-            mc = max(m, mx)
-            if mc != -np.inf and (m == -np.inf or (mc - m) * sc > RESCALE_LOG2):
-                alpha = np.float32(np.exp2(np.float32((m - mc) * sc)))
-                m = mc
+            if mx > m_thr:
+                alpha = np.float32(np.exp2(np.float32((m - mx) * sc)))
+                m = mx
+                m_thr = np.float32(mx + gap)
                 l = np.float32(l * alpha)
                 o = (o * alpha).astype(np.float32)
             nmsc = np.float32(0.0) if m == -np.inf else np.float32(-m * sc)
