@@ -391,18 +391,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         }
       }
       // row max over the lane's 32 scores as a tree of three-input maxima (v_max3_f32)
-      float m1[11];
+      // (30 scores in 10 triples, then those 10 and the last 2 scores in 4 triples, then 4 -> 1:
+      // 16 instructions)
+      float m1[12];
 #pragma unroll
       for (int j = 0; j < 10; ++j) {
         const int a = 3 * j, b = 3 * j + 1, c = 3 * j + 2;
         m1[j] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[c >> 4][c & 15]);
       }
-      m1[10] = fmaxf(s[1][14], s[1][15]);
-      const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
-      const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
-      const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
-      const float m2d = fmaxf(m1[9], m1[10]);
-      return partner_max(fmaxf(fmaxf(fmaxf(m2a, m2b), m2c), m2d));
+      m1[10] = s[1][14];
+      m1[11] = s[1][15];
+      float m2[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m2[j] = fmaxf(fmaxf(m1[3 * j], m1[3 * j + 1]), m1[3 * j + 2]);
+      return partner_max(fmaxf(fmaxf(fmaxf(m2[0], m2[1]), m2[2]), m2[3]));
     };
     // P = exp2(s * sc - m * sc) as bf16 for 16-key step j; l += its row sums
     auto softmax_step = [&](const floatx16 (&s)[2], int j, float nmsc, bf16x8& pj) {
