@@ -243,7 +243,11 @@ psb_status psb_blockdiag_attn_fwd_noalloc(const void* q, const void* k, const vo
  *
  * psb_blockdiag_attn_plan writes the tile schedule for (doc_ids, B, Hq, Hkv, L,
  * S, seq_start, enable_gqa) into `workspace` (size from
- * psb_blockdiag_attn_fwd_workspace_size).  D is checked only for support.
+ * psb_blockdiag_attn_fwd_workspace_size).  The row tiles are ordered longest key
+ * range first, or kept in row order when even the longest is short next to the share
+ * of all tiles each concurrent attention workgroup gets; that count comes from the
+ * current device's compute units and D (which is otherwise checked only for
+ * support).  The order affects speed only, never results.
  *
  * psb_blockdiag_attn_fwd_planned launches the attention kernel alone; it reads
  * the schedule from `workspace`, which must hold a plan made with the same

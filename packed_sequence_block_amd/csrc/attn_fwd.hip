@@ -31,6 +31,7 @@
 #include <float.h>
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "attn_common.h"
@@ -570,13 +571,30 @@ psb_status check_attn_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64
   return PSB_OK;
 }
 
-psb_status plan_impl(const int32_t* doc_ids, int64_t B, int64_t L, int64_t S, int64_t seq_start,
+// Workgroups of the attention kernel that run at once on the current device: compute units
+// x its workgroups per CU (two at D = 128, three at D = 64, set by its registers); 0 when
+// the device cannot be queried (the plan then always orders longest first).
+int32_t concurrent_slots(int64_t D) {
+  static std::atomic<int32_t> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int32_t n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+    n = v;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n * (D == 64 ? 3 : 2);
+}
+
+psb_status plan_impl(const int32_t* doc_ids, int64_t B, int64_t L, int64_t S, int64_t D, int64_t seq_start,
                      const AttnGeometry& geo, void* workspace, size_t workspace_bytes, hipStream_t s) {
   if (doc_ids == nullptr || workspace == nullptr || !aligned16(workspace)) return PSB_ERR_INVALID_ARG;
   if (workspace_bytes < (size_t)schedule_bytes(B, L, geo.nr)) return PSB_ERR_CAPACITY;
   const ScheduleBuffers buf = schedule_carve(workspace, B, L, geo.nr);
-  if (launch_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, (int32_t)geo.nr, buf, s) !=
-      hipSuccess)
+  if (launch_schedule(doc_ids, (int32_t)B, (int32_t)S, (int32_t)L, (int32_t)seq_start, (int32_t)geo.nr,
+                      concurrent_slots(D), (int32_t)geo.units, buf, s) != hipSuccess)
     return PSB_ERR_HIP;
   return PSB_OK;
 }
@@ -678,8 +696,9 @@ PSB_API psb_status psb_blockdiag_prepare(const int32_t* cu_seqlens, int64_t cu_r
   ScheduleBuffers buf = {nullptr, nullptr, nullptr};
   if (plan) buf = schedule_carve(workspace, B, L, geo.nr);
   const hipError_t e = launch_prepare(cu_seqlens, cu_row_stride, (int32_t)n_docs, (int32_t)B, (int32_t)S,
-                                      plan ? (int32_t)L : 0, (int32_t)seq_start, (int32_t)geo.nr, doc_ids_out,
-                                      seg_cu_out, seg_n_out, buf, status_word, as_stream(stream));
+                                      plan ? (int32_t)L : 0, (int32_t)seq_start, (int32_t)geo.nr,
+                                      concurrent_slots(D), (int32_t)geo.units, doc_ids_out, seg_cu_out,
+                                      seg_n_out, buf, status_word, as_stream(stream));
   return e == hipSuccess ? PSB_OK : PSB_ERR_HIP;
 }
 
@@ -690,7 +709,7 @@ PSB_API psb_status psb_blockdiag_attn_plan(const int32_t* doc_ids, int64_t B, in
   const psb_status st = check_attn_shape(B, Hq, Hkv, L, S, D, seq_start, enable_gqa, &geo);
   if (st != PSB_OK) return st;
   if (B == 0 || Hq == 0 || L == 0) return PSB_OK;
-  return plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, as_stream(stream));
+  return plan_impl(doc_ids, B, L, S, D, seq_start, geo, workspace, workspace_bytes, as_stream(stream));
 }
 
 PSB_API psb_status psb_blockdiag_attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -751,7 +770,7 @@ psb_status fwd_whole(const void* q, const void* k, const void* v, const int32_t*
   if (qs[2] < D || kvs[2] < D) return PSB_ERR_SHAPE;
   if (kvs[2] * 2 * kKeysPerTile >= INT32_MAX) return PSB_ERR_SHAPE;  // tile offsets are 32-bit
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PSB_ERR_INVALID_ARG;
-  st = plan_impl(doc_ids, B, L, S, seq_start, geo, workspace, workspace_bytes, s);
+  st = plan_impl(doc_ids, B, L, S, D, seq_start, geo, workspace, workspace_bytes, s);
   if (st != PSB_OK) return st;
   st = run_impl(q, k, v, doc_ids, B, Hq, Hkv, L, S, D, q_strides, kv_strides, seq_start, 0, S, scale, geo, out,
                 nullptr, workspace, workspace_bytes, nullptr, s);

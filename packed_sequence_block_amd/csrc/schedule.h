@@ -22,7 +22,8 @@ static_assert(sizeof(TileRecord) == 64, "tile record is 64 bytes");
 
 // Device tables, carved out of the caller's workspace.
 //   blk_lo/blk_hi [B * nblk]: key range of each 32-row query block (hi <= lo: no valid row)
-//   work [T]:                 tile records, longest key range first
+//   work [T]:                 tile records, longest key range first (or in row order, see
+//                             launch_schedule)
 struct ScheduleBuffers {
   int32_t* blk_lo;
   int32_t* blk_hi;
@@ -47,15 +48,20 @@ inline ScheduleBuffers schedule_carve(void* ws, int64_t B, int64_t L, int64_t nr
   return s;
 }
 
+// slots: workgroups the attention kernel runs at once (0: always longest first); units:
+// head units per row tile (the plan picks row order when the longest record is short next
+// to a slot's share of all records x units)
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
-                           int32_t nr, const ScheduleBuffers& buf, hipStream_t stream);
+                           int32_t nr, int32_t slots, int32_t units, const ScheduleBuffers& buf,
+                           hipStream_t stream);
 
 // Document ids, run boundaries and the plan above for B rows at once, from boundaries
 // cu [B][n_docs + 1] (row stride cu_stride): one launch when B * ceil(L / 32) <= 2048,
 // else two.
 hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
-                          int32_t seq_start, int32_t nr, int32_t* ids, int32_t* seg_cu, int32_t* seg_n,
-                          const ScheduleBuffers& buf, int32_t* status, hipStream_t stream);
+                          int32_t seq_start, int32_t nr, int32_t slots, int32_t units, int32_t* ids,
+                          int32_t* seg_cu, int32_t* seg_n, const ScheduleBuffers& buf, int32_t* status,
+                          hipStream_t stream);
 
 // Backward key side: tiles of kKeyTile keys of the window [kv_start, kv_start + kv_len),
 // each with the local query rows that see its keys.  A tile whose row range is much longer

@@ -13,7 +13,11 @@
 // around the first true one (3 dependent steps for S = 64K).
 // Kernel 2 (one workgroup) merges NR blocks into a row tile record, and orders
 // the records by descending key-range length (counting sort), so the attention
-// workgroups take the longest tiles first.
+// workgroups take the longest tiles first.  When even the longest record is short next
+// to the share of the work each concurrent workgroup slot gets (4 x longest x slots <=
+// all tiles x head units), the tail that longest-first avoids cannot arise, and the
+// records keep row order instead: consecutive workgroups then read the same documents'
+// keys, which stay in L2.
 #include "psb_internal.h"
 #include "schedule.h"
 
@@ -128,19 +132,38 @@ __device__ void bucket_offsets_desc(int32_t* hist, int32_t* wsum) {
 
 // Records of all B * ntile_row row tiles into work[], longest key range first: a counting
 // sort over the tile count of each record's range (bucket kBuckets - 1 collects the
-// rest), done by one workgroup of NT threads.  hist: kBuckets ints of LDS, wsum: NT / 64.
+// rest), done by one workgroup of NT threads; or in row order when the longest record is
+// short next to a workgroup slot's share (slots = workgroups the attention kernel runs at
+// once, 0 = always longest first; units = head units per row tile).  hist: kBuckets ints
+// of LDS, wsum: NT / 64.
 template <int NT>
 __device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_t B, int32_t nblk, int32_t nr,
-                            int32_t ntile_row, TileRecord* __restrict__ work, int32_t* hist, int32_t* wsum) {
+                            int32_t ntile_row, int32_t slots, int32_t units, TileRecord* __restrict__ work,
+                            int32_t* hist, int32_t* wsum) {
+  __shared__ unsigned long long s_total;
+  __shared__ int32_t s_longest;
   const int tid = threadIdx.x;
   const int32_t T = B * ntile_row;
   for (int i = tid; i < kBuckets; i += NT) hist[i] = 0;
+  if (tid == 0) { s_total = 0ull; s_longest = 0; }
   __syncthreads();
+  unsigned long long total = 0ull;
+  int32_t longest = 0;
   for (int32_t t = tid; t < T; t += NT) {
     const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
-    atomicAdd(&hist[min(tile_iters(r.lo, r.hi), kBuckets - 1)], 1);
+    const int32_t n = tile_iters(r.lo, r.hi);
+    total += (unsigned long long)n;
+    longest = max(longest, n);
+    atomicAdd(&hist[min(n, kBuckets - 1)], 1);
   }
+  atomicAdd(&s_total, total);
+  atomicMax(&s_longest, longest);
   __syncthreads();
+  if (slots > 0 && 4ull * (unsigned long long)s_longest * (unsigned long long)slots <=
+                       s_total * (unsigned long long)units) {  // uniform
+    for (int32_t t = tid; t < T; t += NT) work[t] = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
+    return;
+  }
   bucket_offsets_desc<NT>(hist, wsum);
   for (int32_t t = tid; t < T; t += NT) {
     const TileRecord r = make_record(blk_lo, blk_hi, t, nblk, nr, ntile_row);
@@ -152,11 +175,12 @@ __device__ void order_tiles(const int32_t* blk_lo, const int32_t* blk_hi, int32_
 __global__ void __launch_bounds__(kSortThreads) tile_order_kernel(const int32_t* __restrict__ blk_lo,
                                                                   const int32_t* __restrict__ blk_hi,
                                                                   int32_t B, int32_t nblk, int32_t nr,
-                                                                  int32_t ntile_row,
+                                                                  int32_t ntile_row, int32_t slots,
+                                                                  int32_t units,
                                                                   TileRecord* __restrict__ work) {
   __shared__ int32_t hist[kBuckets];
   __shared__ int32_t wsum[kSortThreads / kWave];
-  order_tiles<kSortThreads>(blk_lo, blk_hi, B, nblk, nr, ntile_row, work, hist, wsum);
+  order_tiles<kSortThreads>(blk_lo, blk_hi, B, nblk, nr, ntile_row, slots, units, work, hist, wsum);
 }
 
 // ---- key side (backward dK / dV) -----------------------------------------------------
@@ -374,8 +398,8 @@ __global__ void __launch_bounds__(kPrepThreads) prepare_kernel(
     const int32_t* __restrict__ cu_all, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
     int32_t seq_start, int32_t nblk, int32_t id_chunks, int32_t range_groups, int32_t* __restrict__ ids,
     int32_t* __restrict__ seg_cu, int32_t* __restrict__ seg_n, int32_t* __restrict__ blk_lo,
-    int32_t* __restrict__ blk_hi, int32_t* __restrict__ status, int32_t nr, int32_t ntile_row,
-    TileRecord* __restrict__ work, int32_t plan_in_grid) {
+    int32_t* __restrict__ blk_hi, int32_t* __restrict__ status, int32_t nr, int32_t ntile_row, int32_t slots,
+    int32_t units, TileRecord* __restrict__ work, int32_t plan_in_grid) {
   constexpr int kCuStage = 4096;
   __shared__ int32_t scu[kCuStage];
   __shared__ int32_t wsum[kPrepThreads / kWave];
@@ -436,7 +460,7 @@ __global__ void __launch_bounds__(kPrepThreads) prepare_kernel(
       block_range_from_cu(cu, n_docs, w % nblk, L, seq_start, plo[w], phi[w]);
     }
     __syncthreads();
-    order_tiles<kPrepThreads>(plo, phi, B, nblk, nr, ntile_row, work, hist, wsum);
+    order_tiles<kPrepThreads>(plo, phi, B, nblk, nr, ntile_row, slots, units, work, hist, wsum);
     return;
   }
   // segments of row b
@@ -528,7 +552,8 @@ __global__ void __launch_bounds__(256) shard_window_kernel(const int32_t* __rest
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t L, int32_t seq_start,
-                           int32_t nr, const ScheduleBuffers& buf, hipStream_t stream) {
+                           int32_t nr, int32_t slots, int32_t units, const ScheduleBuffers& buf,
+                           hipStream_t stream) {
   const int32_t nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
   const int32_t total = B * nblk;
   const int waves_per_wg = 256 / kWave;
@@ -539,7 +564,7 @@ hipError_t launch_schedule(const int32_t* doc_ids, int32_t B, int32_t S, int32_t
   if (e != hipSuccess) return e;
   const int32_t ntile_row = (nblk + nr - 1) / nr;
   tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
-                                                                buf.work);
+                                                                slots, units, buf.work);
   return hipGetLastError();
 }
 
@@ -584,8 +609,9 @@ PSB_API psb_status psb_shard_kv_window_start(const int32_t* doc_ids, int64_t B, 
 namespace psb {
 
 hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, int32_t B, int32_t S, int32_t L,
-                          int32_t seq_start, int32_t nr, int32_t* ids, int32_t* seg_cu, int32_t* seg_n,
-                          const ScheduleBuffers& buf, int32_t* status, hipStream_t stream) {
+                          int32_t seq_start, int32_t nr, int32_t slots, int32_t units, int32_t* ids,
+                          int32_t* seg_cu, int32_t* seg_n, const ScheduleBuffers& buf, int32_t* status,
+                          hipStream_t stream) {
   const int32_t nblk = (L + kRowsPerBlock - 1) / kRowsPerBlock;
   const int32_t id_chunks = (S + kPrepThreads - 1) / kPrepThreads;
   const int64_t waves_per_wg = kPrepThreads / kWave;
@@ -597,11 +623,11 @@ hipError_t launch_prepare(const int32_t* cu, int64_t cu_stride, int32_t n_docs, 
   const int64_t grid = (int64_t)B * id_chunks + range_groups + B + (fused ? 1 : 0);
   prepare_kernel<<<dim3((unsigned)grid), dim3(kPrepThreads), 0, stream>>>(
       cu, cu_stride, n_docs, B, S, L, seq_start, nblk, id_chunks, range_groups, ids, seg_cu, seg_n, buf.blk_lo,
-      buf.blk_hi, status, nr, ntile_row, buf.work, fused ? 1 : 0);
+      buf.blk_hi, status, nr, ntile_row, slots, units, buf.work, fused ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nblk == 0 || fused) return e;
   tile_order_kernel<<<dim3(1), dim3(kSortThreads), 0, stream>>>(buf.blk_lo, buf.blk_hi, B, nblk, nr, ntile_row,
-                                                                buf.work);
+                                                                slots, units, buf.work);
   return hipGetLastError();
 }
 

@@ -2,9 +2,11 @@
 
 The plan is the step between the document ids and the attention kernel: for every
 32-row query block, the key range [start of the first valid row's document, last
-valid row + 1), and the list of row-tile records ordered by key-range length.  Its
-tables are checked directly here, exactly (integers) except for the order of
-records with equal length, which the counting sort leaves open.
+valid row + 1), and the list of row-tile records ordered by key-range length (or
+in row order when the longest record is short next to the share of all records that
+each concurrent workgroup slot of the attention kernel gets).  Its tables are checked
+directly here, exactly (integers) except for the order of records with equal length,
+which the counting sort leaves open.
 """
 
 import ctypes
@@ -67,7 +69,12 @@ def check_plan(lib, ids_np, Hq, Hkv, L, seq_start):
     check_plan_words(run_plan(lib, ids_np, Hq, Hkv, L, seq_start), ids_np, Hq, Hkv, L, seq_start)
 
 
-def check_plan_words(words, ids_np, Hq, Hkv, L, seq_start):
+def concurrent_slots(D=128):
+    """Workgroups the attention kernel runs at once: CUs x 2 at D = 128, x 3 at D = 64."""
+    return torch.cuda.get_device_properties(0).multi_processor_count * (2 if D == 128 else 3)
+
+
+def check_plan_words(words, ids_np, Hq, Hkv, L, seq_start, D=128):
     """The plan tables in a workspace (as int32 words) against the definition."""
     B = ids_np.shape[0]
     group = Hq // Hkv
@@ -83,7 +90,7 @@ def check_plan_words(words, ids_np, Hq, Hkv, L, seq_start):
     assert np.array_equal(got_hi, hi), "block hi"
     rec = words[2 * off:2 * off + 16 * B * ntile_row].reshape(-1, 16)
     seen = set()
-    iters = []
+    iters, full_iters, order = [], [], []
     for r in rec:
         b, rt = int(r[0]), int(r[1])
         assert 0 <= b < B and 0 <= rt < ntile_row
@@ -97,9 +104,17 @@ def check_plan_words(words, ids_np, Hq, Hkv, L, seq_start):
         want_hi = int(bhi[nz].max()) if nz.any() else 0
         assert (int(r[2]), int(r[3])) == (want_lo, want_hi), (b, rt)
         assert np.array_equal(r[4:8], blo) and np.array_equal(r[8:12], bhi), (b, rt)
-        iters.append(min(-(-(want_hi - want_lo) // KEYS) if want_hi > want_lo else 0, 2047))
+        n = -(-(want_hi - want_lo) // KEYS) if want_hi > want_lo else 0
+        full_iters.append(n)
+        iters.append(min(n, 2047))
+        order.append(b * ntile_row + rt)
     assert len(seen) == B * ntile_row, "every row tile exactly once"
-    assert all(a >= b for a, b in zip(iters, iters[1:])), "longest key range first"
+    units = Hq // nh
+    if 4 * max(full_iters) * concurrent_slots(D) <= sum(full_iters) * units:
+        assert order == list(range(B * ntile_row)), "row order"
+    else:
+        assert all(a >= b for a, b in zip(iters, iters[1:])), "longest key range first"
+    return order
 
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
@@ -107,6 +122,17 @@ def test_named_layouts(lib, c):
     lay = make_layout(c)
     say("plan cfg", c)
     check_plan(lib, oracle_doc_ids(lay), lay.Hq, lay.Hkv, lay.L, lay.seq_start)
+
+
+@pytest.mark.parametrize("c,row_order", [(2, False), (3, False), (4, True)])
+def test_order_choice(lib, c, row_order):
+    # short documents against a large grid keep row order (workload 4); long single
+    # records next to a small grid are ordered longest first (workloads 2, 3)
+    lay = make_layout(c)
+    say("plan order cfg", c)
+    order = check_plan_words(run_plan(lib, oracle_doc_ids(lay), lay.Hq, lay.Hkv, lay.L, lay.seq_start),
+                             oracle_doc_ids(lay), lay.Hq, lay.Hkv, lay.L, lay.seq_start)
+    assert (order == sorted(order)) == row_order
 
 
 def random_ids(rng, B, S):

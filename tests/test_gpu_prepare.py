@@ -51,7 +51,7 @@ def check(psb, rows, S, L, s0, Hq, Hkv, D):
         assert n_c[b] == len(want) - 1 and np.array_equal(seg_c[b, :n_c[b] + 1], want), f"segments row {b}"
     if L > 0:
         words = ws.cpu().numpy().view(np.int32)
-        check_plan_words(words, ids_c, Hq, Hkv, L, s0)
+        check_plan_words(words, ids_c, Hq, Hkv, L, s0, D)
     return ids, ws
 
 
