@@ -20,9 +20,10 @@
 //   dkdv_kernel   key-stationary: a wave owns 32 keys of one kv head (K held in VGPRs
 //                 as an MFMA B operand; V too at D = 64, in LDS at D = 128), a workgroup
 //                 128 keys, two waves per SIMD; it walks every query head of the group and
-//                 the query rows that can see its keys, 32 rows per step, recomputes S and
-//                 dP (lane = key), and accumulates dV^T += dO^T P and dK^T += Q^T dS with
-//                 Q^T / dO^T gathered by transposing LDS reads.  When a 128-key tile is
+//                 the query rows that can see its keys, 32 (D = 128) or 64 (D = 64) rows
+//                 per step, recomputes S and dP (lane = key), and accumulates
+//                 dV^T += dO^T P and dK^T += Q^T dS with Q^T / dO^T gathered by
+//                 transposing LDS reads.  When a 128-key tile is
 //                 seen by many rows, the plan splits those rows into chunks that run as
 //                 separate items writing fp32 partial dK / dV, and dkdv_reduce_kernel
 //                 adds each tile's chunks in chunk order.
@@ -350,10 +351,12 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 // has no rows).  Rows are local query rows [0, L) at global positions seq_start + r.
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
-  // 32 query rows per step, two waves per SIMD.  At D = 128 a wave's V rows wait in LDS
-  // (its own 32 rows, read back as the dP MFMA operand) instead of 32 VGPRs, which keeps
-  // the wave within 256 registers next to its 128 dK / dV accumulators.
-  constexpr int kRowsPerStep = 32;
+  // Two waves per SIMD.  At D = 128: 32 query rows per step, and a wave's V rows wait in
+  // LDS (its own 32 rows, read back as the dP MFMA operand) instead of 32 VGPRs, which
+  // keeps the wave within 256 registers next to its 128 dK / dV accumulators.  At D = 64:
+  // 64 rows per step (two independent 32-row halves), half the barriers and load waits per
+  // flop of 32-row steps.
+  constexpr int kRowsPerStep = D == 64 ? 64 : 32;
   constexpr bool VLDS = D == 128;
   constexpr int VROW = D + 8;  // padded V row: the 16 rows of one b128 read on distinct banks
   constexpr int KS = D / 16;
