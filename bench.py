@@ -14,7 +14,8 @@ Headline workload (default --config 5): the long mixed row (B=1, S=L=65536,
 Hq=64, Hkv=4, D=64, 80% uniform[64, 1024] / 20% uniform[8192, 24576] document
 lengths, seed 5), the largest of the five workloads.  About 150 ms of untimed
 steps warm the device up (its clock ramps under load), then W warmup steps run
-and exactly K steps are timed
+and exactly K steps are timed (K by default at least 30 and enough to last
+>= 100 ms)
 by the wall clock between two device synchronizations; inside that window an
 event pair on the launch stream brackets every attention launch, so
 `roofline.kernel_ms` (the mean of those launch durations) is measured over the
@@ -417,7 +418,8 @@ def sub_record(psb, lib, c, dev, args, legs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 30, and enough to last >= 100 ms)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--sub-configs", default="2,3,4", help="comma-separated workloads also measured ('' for none)")
@@ -463,6 +465,10 @@ def main():
         pb.prepare()
         pb.attention()
     torch.cuda.synchronize(dev)
+    # a burst of a few ms right after a synchronization runs partly at a lower clock:
+    # unless told otherwise, time enough steps to last >= 100 ms
+    if args.steps is None:
+        args.steps = max(30, int(100.0 / max(est, 1e-3)) + 1)
     ms_step, kernel_ms, per_launch = pb.time_steps(args.steps)
     assert kernel_ms <= ms_step, f"attention launches ({kernel_ms} ms) longer than the step ({ms_step} ms)"
     value, achieved = _rates(lay, ms_step, kernel_ms)
