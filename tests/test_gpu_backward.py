@@ -223,3 +223,46 @@ def test_long_documents_split_key_tiles(psb):
     torch.cuda.synchronize()
     for a, b in zip(grads, again):
         assert torch.equal(a, b)
+
+
+def _full_size_grads(psb, lay, seed):
+    q, k, v = make_qkv(lay)
+    ids = oracle_doc_ids(lay)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    dev = "cuda"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    idd = torch.as_tensor(ids, dtype=torch.int32).to(dev)
+    out, lse, ws = psb.blockdiag_attn_fwd_lse(qd, kd, vd, idd, lay.seq_start, None, lay.enable_gqa)
+    dq, dk, dv = psb.blockdiag_attn_bwd(qd, kd, vd, out, dout.to(dev), lse, idd, ws, lay.seq_start, None,
+                                        lay.enable_gqa)
+    torch.cuda.synchronize()
+    return q, k, v, ids, dout, dq.cpu(), dk.cpu(), dv.cpu()
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_whole_gradients(psb, c):
+    # every element of dq, dk, dv at full size against the oracle (one batch row at a time)
+    lay = make_layout(c)
+    say("bwd whole gradients", lay.name)
+    q, k, v, ids, dout, dq, dk, dv = _full_size_grads(psb, lay, 60 + c)
+    for b in range(lay.B):
+        rq, rk, rv = oracle.blockdiag_attn_bwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], dout[b:b + 1],
+                                               np.asarray(ids[b:b + 1]), lay.seq_start, None, lay.enable_gqa)
+        check_grad(dq[b:b + 1], rq, f"{lay.name} row {b} dq")
+        check_grad(dk[b:b + 1], rk, f"{lay.name} row {b} dk")
+        check_grad(dv[b:b + 1], rv, f"{lay.name} row {b} dv")
+
+
+def test_whole_gradients_cfg5_kv_head(psb):
+    # workload 5 (S = 65536): every element of the gradients of kv head 1 and its 16 query
+    # heads (heads never mix, so the oracle on that slice alone gives them)
+    lay = make_layout(5)
+    g, G = 1, lay.Hq // lay.Hkv
+    say("bwd whole gradients", lay.name, "kv head", g)
+    q, k, v, ids, dout, dq, dk, dv = _full_size_grads(psb, lay, 65)
+    hs = slice(g * G, (g + 1) * G)
+    rq, rk, rv = oracle.blockdiag_attn_bwd(q[:, hs], k[:, g:g + 1], v[:, g:g + 1], dout[:, hs], np.asarray(ids),
+                                           lay.seq_start, None, True)
+    check_grad(dq[:, hs], rq, f"{lay.name} kv head {g} dq")
+    check_grad(dk[:, g:g + 1], rk, f"{lay.name} kv head {g} dk")
+    check_grad(dv[:, g:g + 1], rv, f"{lay.name} kv head {g} dv")
