@@ -68,9 +68,9 @@ struct AttnParams {
   int64_t mask_sb, mask_ss;
 };
 
-// the running row max is only moved (and O, l rescaled) when a tile's max exceeds
-// it by more than 2^8 in the exp2 domain; until then p <= 2^8, harmless in fp32/bf16
-constexpr float kRescaleLog2 = 8.0f;
+// the exp2 offset is only moved (and O, l rescaled) when the P of a 64-key tile sums to
+// more than 2^8 in some lane; until then every p < 2^8, harmless in fp32 / bf16
+constexpr float kRetuneSum = 256.0f;
 
 // LDS tiles, 64 keys each, rows of D bf16 with no padding; 16-byte chunk c of row r is
 // stored at chunk c ^ f(r), so that every read is free of bank conflicts (64 banks of 4
@@ -298,10 +298,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     floatx16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16;
-    // running max m (raw score units), the exp2 offset -m sc and the rescale threshold
-    // m + 2^8 / sc; all start at "no key yet" (-inf, 0, -inf)
-    float m_run = -INFINITY, l_run = 0.f, nmsc = 0.f, m_thr = -INFINITY;
-    const float thr_gap = kRescaleLog2 / sc;
+    // p = exp2(s sc + nmsc) with the exp2 offset nmsc = -m sc for the row max m last taken,
+    // l the running sum of p.  nmsc starts at FLT_MAX: a row's first finite score then gives
+    // p = inf and forces the exact max, while masked scores (-inf) still give 0.
+    float l_run = 0.f, nmsc = FLT_MAX;
 
     // S^T of one 64-key tile (both 32-key blocks, chains interleaved) from K stage `st`;
     // operands read two k-steps ahead of their MFMAs
@@ -378,22 +378,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
           }
       }
     };
-    auto mask_max = [&](int32_t kt, floatx16 (&s)[2]) {
-      const bool full = DENSE || (single && kt >= w_lo && (kt + 63) <= wq0);
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int32_t e = kt + 32 * kb + 4 * h - kshift;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
-            s[kb][i] = (rel <= span) ? s[kb][i] : -INFINITY;
-          }
-        }
-      }
-      // row max over the lane's 32 scores as a tree of three-input maxima (v_max3_f32)
-      // (30 scores in 10 triples, then those 10 and the last 2 scores in 4 triples, then 4 -> 1:
-      // 16 instructions)
+    // row max of the tile (retune path only): the lane's 32 scores as a tree of
+    // three-input maxima (v_max3_f32), then the partner lane's
+    auto tile_max = [&](const floatx16 (&s)[2]) {
       float m1[12];
 #pragma unroll
       for (int j = 0; j < 10; ++j) {
@@ -407,34 +394,77 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       for (int j = 0; j < 4; ++j) m2[j] = fmaxf(fmaxf(m1[3 * j], m1[3 * j + 1]), m1[3 * j + 2]);
       return partner_max(fmaxf(fmaxf(fmaxf(m2[0], m2[1]), m2[2]), m2[3]));
     };
-    // P = exp2(s * sc - m * sc) as bf16 for 16-key step j; l += its row sums
-    auto softmax_step = [&](const floatx16 (&s)[2], int j, float nmsc, bf16x8& pj) {
+    auto mask_tile = [&](int32_t kt, floatx16 (&s)[2]) {
+      const bool full = DENSE || (single && kt >= w_lo && (kt + 63) <= wq0);
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int32_t e = kt + 32 * kb + 4 * h - kshift;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t rel = (uint32_t)(e + (i >> 2) * 8 + (i & 3));
+            s[kb][i] = (rel <= span) ? s[kb][i] : -INFINITY;
+          }
+        }
+      }
+    };
+    // P = exp2(s sc + nmsc) as bf16 for 16-key step j; acc += its sum in this lane (of the
+    // bf16 values P V uses)
+    auto softmax_step = [&](const floatx16 (&s)[2], int j, bf16x8& pj, float& acc) {
       bf16x2 pp[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t], sc, nmsc));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t + 1], sc, nmsc));
         pp[t] = cvt_bf16x2(e0, e1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, l_run, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, acc, false);
       }
       pj = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    // softmax(t) fused with PV(t): P for 16-key step j is produced while the MFMAs of
-    // step j-1 run (about 6 VALU ops per MFMA); V^T operands are read one step ahead.
-    // A hard scheduling barrier between steps keeps the interleaving.
     // V^T operand of 16-key step j, d block db: rows 16 j + ... and 8 rows on, same chunks
     auto vtr = [&](const char* vb, int j, int db) {
       const char* a = vb + 16 * j * ROWB + (vt_rd ^ (64 * db));
       return vtr_pair_at(a, a + 8 * ROWB);
     };
+    // The offset moves (O and l are rescaled) when some lane's P for the tile sums to
+    // more than 2^8: nmsc becomes -m sc for the tile's row max m wherever that lies above
+    // the current offset.  A lane whose sum passed 2^8 has some p > 2^3, so there
+    // m sc + nmsc > 3 and it moves; alpha = 2^(new - old) < 1, and exactly 0 at a row's first
+    // finite key (nmsc starts at FLT_MAX, with O and l still 0).
+    auto retune = [&](const floatx16 (&s)[2]) {
+      const float mx = tile_max(s);
+      const float nm = -mx * sc;
+      const bool grow = nm < nmsc;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(nm - nmsc) : 1.f;
+      nmsc = grow ? nm : nmsc;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    };
+    // softmax and P V of one tile: all of the tile's P with the offset in force (V^T operands
+    // of the first step read meanwhile), one wave-uniform test of the lane sums, then the
+    // P V MFMAs with the next step's V^T operands read one step ahead.  With two or three
+    // waves per SIMD the other waves' exp2 work runs under these MFMAs.
     auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf) {
       const char* vb = (const char*)vbuf;
       bf16x8 pk[4];
       bf16x8 va[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) va[db] = vtr(vb, 0, db);
-      softmax_step(s, 0, nmsc, pk[0]);
+      float ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) softmax_step(s, j, pk[j], ls);
+      __builtin_amdgcn_sched_barrier(0);
+      if (__builtin_amdgcn_ballot_w64(ls > kRetuneSum) != 0) {  // wave-uniform (scalar) test
+        retune(s);
+        ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) softmax_step(s, j, pk[j], ls);
+      }
+      l_run += ls;
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -444,36 +474,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk[j], o[db], 0, 0, 0);
           if (j < 3) va[db] = vtr(vb, j + 1, db);
         }
-        if (j < 3) {
-          softmax_step(s, j + 1, nmsc, pk[j + 1]);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 24 / DB, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 3 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
     };
-    // lazy running max: m moves (and O, l are rescaled) only when the tile max exceeds
-    // it by more than 2^8 in the exp2 domain, i.e. exceeds m_thr (-inf until the first
-    // key, so the first finite score always moves it; alpha is then exp2(-inf) = 0 on an
-    // O and l that are still 0)
-    auto rescale = [&](float mx) {
-      const bool grow = mx > m_thr;
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * sc) : 1.f;
-      m_run = grow ? mx : m_run;
-      m_thr = grow ? mx + thr_gap : m_thr;
-      nmsc = grow ? -mx * sc : nmsc;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    };
-
     // ---- tile loop ----------------------------------------------------------------------
     // Step t reads K(t), V(t) from sK0 / sV0 (t even) or sK1 / sV1 (t odd), loaded straight
     // into LDS during step t-1, and starts the loads of K(t+1), V(t+1) into the other pair.
@@ -498,8 +507,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       qk(kcur, st_s, rkn, knext, rvn, vnext);
       if (more) load_mask(kt + kKeysPerTile, mnext);
       apply_mask(st_s, mcur);
-      const float mx = mask_max(kt, st_s);
-      if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) rescale(mx);  // wave-uniform (scalar) test
+      mask_tile(kt, st_s);
       softmax_pv(st_s, vcur);
     };
     int32_t t = 0;
@@ -513,9 +521,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     const float l_tot = partner_sum(l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     if (p.lse != nullptr && row_in && h == 0) {
-      // sum_k exp(scale s_k) = 2^(m sc) * l in the exp2 domain of the loop (m_run is the
-      // same in both partner lanes); a row without keys gets -inf
-      const float lse2 = (l_tot > 0.f) ? m_run * sc + __log2f(l_tot) : -INFINITY;
+      // sum_k exp(scale s_k) = 2^(-nmsc) * l in the exp2 domain of the loop (nmsc is the
+      // same in both partner lanes, and finite once the row has a key); a row without keys
+      // gets -inf
+      const float lse2 = (l_tot > 0.f) ? __log2f(l_tot) - nmsc : -INFINITY;
       p.lse[((int64_t)b * p.Hq + hq) * p.L + row_local] = lse2 * 0.69314718055994531f;
     }
 #pragma unroll

@@ -1,20 +1,26 @@
 """A CPU model of the forward kernel's per-row softmax arithmetic, against the oracle.
 
-The forward kernel walks 64-key tiles and keeps, per query row, a running maximum m
-of the raw scores, a running sum l and an fp32 accumulator o (online softmax in the
-exp2 domain with sc = |scale| * log2(e)):
-  * masked scores become -inf; the tile maximum is taken over raw scores;
-  * m moves only when the tile maximum exceeds the threshold m + 2^8 / sc (float32,
-    -inf until the first key); then m' = tile maximum and l, o are multiplied by
-    exp2((m - m') sc);
-  * p = exp2(s sc - m sc) (one fused multiply-add), rounded to bf16; l adds the bf16
-    p, o adds p times v;
-  * the output is o / l (0 when l == 0), rounded to bf16.
+The forward kernel walks 64-key tiles and keeps, per query row, an exp2 offset nmsc,
+a running sum l and an fp32 accumulator o (online softmax in the exp2 domain with
+sc = |scale| * log2(e)):
+  * masked scores become -inf;
+  * p = exp2(s sc + nmsc) (one fused multiply-add), rounded to bf16, for the whole tile;
+  * if the bf16 p held by one lane (half of the tile's keys: key % 8 < 4, or the rest)
+    sum to more than 2^8, the offset is retuned: with m the tile's maximum raw score,
+    nmsc' = -m sc replaces nmsc wherever it is smaller; l and o are multiplied by
+    exp2(nmsc' - nmsc) and the tile's p are recomputed;
+  * nmsc starts at FLT_MAX, so that a row's first finite score gives p = inf and forces
+    the exact maximum (masked scores still give exp2(-inf) = 0);
+  * l adds the bf16 p, o adds p times v; the output is o / l (0 when l == 0), rounded
+    to bf16.
 A negative scale flips the sign of q; sc is held at least at the smallest normal
 float, so that scale = 0 gives equal weights instead of exp2(-inf * 0) = NaN on the
 masked keys.  This model runs the same steps in numpy float32 (the MFMA dot products
 in float32 too, in another summation order) and must meet the oracle's tolerance;
 with sc = 0 allowed through it produces NaN, which is why the kernel holds sc up.
+(The kernel takes the retune decision for a whole wave of 32 rows at once; a retune
+that another row asked for moves this row's offset only when its maximum lies above
+it, which is as exact.)
 """
 
 import numpy as np
@@ -25,9 +31,10 @@ import oracle
 from workloads import make_qkv, random_layout
 
 TILE = 64
-RESCALE_LOG2 = 8.0
+RETUNE_SUM = np.float32(256.0)
 LOG2E = np.float32(1.4426950408889634)
 FLT_MIN = np.float32(np.finfo(np.float32).tiny)
+FLT_MAX = np.float32(np.finfo(np.float32).max)
 
 
 def _bf16(x):
@@ -46,24 +53,22 @@ def model_row(qrow, keys, vals, allowed, scale, clamp=True):
         sc = max(sc, FLT_MIN)
     q = -qrow if np.signbit(np.float32(scale)) and scale != 0 else qrow
     s_all = (keys.astype(np.float32) @ q.astype(np.float32)).astype(np.float32)
-    m = np.float32(-np.inf)
-    m_thr = np.float32(-np.inf)
-    with np.errstate(over="ignore", divide="ignore"):  # 2^8 / sc is +inf at sc = FLT_MIN, as in float32 on the GPU
-        gap = np.float32(np.float32(RESCALE_LOG2) / sc)
+    nmsc = FLT_MAX
     l = np.float32(0.0)
     o = np.zeros(vals.shape[1], dtype=np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         for t0 in range(0, keys.shape[0], TILE):
             s = np.where(allowed[t0:t0 + TILE], s_all[t0:t0 + TILE], np.float32(-np.inf)).astype(np.float32)
-            mx = np.float32(s.max())
-            if mx > m_thr:
-                alpha = np.float32(np.exp2(np.float32((m - mx) * sc)))
-                m = mx
-                m_thr = np.float32(mx + gap)
-                l = np.float32(l * alpha)
-                o = (o * alpha).astype(np.float32)
-            nmsc = np.float32(0.0) if m == -np.inf else np.float32(-m * sc)
+            lane = (np.arange(t0, t0 + len(s)) % 8) < 4
             p = _bf16(np.exp2(_fma32(s, sc, nmsc)))
+            if p[lane].sum(dtype=np.float32) > RETUNE_SUM or p[~lane].sum(dtype=np.float32) > RETUNE_SUM:
+                nm = np.float32(-np.float32(s.max()) * sc)
+                if nm < nmsc:
+                    alpha = np.float32(np.exp2(np.float32(nm - nmsc)))
+                    nmsc = nm
+                    l = np.float32(l * alpha)
+                    o = (o * alpha).astype(np.float32)
+                p = _bf16(np.exp2(_fma32(s, sc, nmsc)))
             l = np.float32(l + p.sum(dtype=np.float32))
             o = (o + p @ vals[t0:t0 + TILE].astype(np.float32)).astype(np.float32)
     inv = np.float32(1.0) / l if l > 0 else np.float32(0.0)
@@ -102,6 +107,21 @@ def test_model_meets_oracle(scale):
     assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
     pad = ids[0, lay.seq_start:lay.seq_start + lay.L] == oracle.PAD_DOC_ID
     assert pad.any() and np.all(got[:, :, pad] == 0)
+
+
+def test_first_key_sets_the_offset():
+    # every score far below zero: an offset that started at 0 would underflow every p
+    # (exp2(-720) = 0) and return zeros; the FLT_MAX start forces the exact maximum first
+    rng = np.random.default_rng(5)
+    S, D = 150, 16
+    qrow = np.full(D, 4.0, dtype=np.float32)
+    keys = np.full((S, D), -8.0, dtype=np.float32)  # q.k = -512 for every key
+    vals = _bf16(rng.standard_normal((S, D)))
+    allowed = np.zeros(S, dtype=bool)
+    allowed[70:131] = True  # the first allowed key sits in the second tile
+    got = model_row(qrow, keys, vals, allowed, 1.0)
+    ref = _bf16(vals[allowed].mean(axis=0))
+    assert np.abs(got - ref).max() <= 2e-2
 
 
 def test_zero_scale_weights_are_exactly_one():
