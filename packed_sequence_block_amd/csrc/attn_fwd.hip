@@ -259,9 +259,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       w_lo = recp->blk_lo[wv / NH];
       if (row_in) dq = p.doc[(int64_t)b * p.S + qpos];
     }
-    // the previous item no longer reads LDS (its operands were consumed by its MFMAs); a
-    // plain barrier leaves the loads above in flight
-    __builtin_amdgcn_s_barrier();
+    // the previous item of this workgroup no longer reads LDS (its operands were consumed by
+    // its MFMAs): a plain barrier, which leaves the loads above in flight; a workgroup's first
+    // item has no predecessor and issues its tile-0 loads at once
+    if (item != blockIdx.x) __builtin_amdgcn_s_barrier();
     issue_k(sK0, tlo);
     issue_v(sV0, tlo);
 
