@@ -125,3 +125,45 @@ def test_gpu_doc_ids_feed_attention(psb):
     out = psb.blockdiag_attn_fwd(q.cuda(), k.cuda(), v.cuda(), ids, 0, None, True)
     ref = oracle.blockdiag_attn(q, k, v, oracle_doc_ids(lay), 0, None, True)
     compare(out, ref, None, "device-ids")
+
+
+def _run_qkv(psb, lay, q, k, v, scale):
+    ids = oracle_doc_ids(lay)
+    out = psb.blockdiag_attn_fwd(q.cuda(), k.cuda(), v.cuda(), torch.as_tensor(ids).cuda(), lay.seq_start,
+                                 scale, lay.enable_gqa)
+    torch.cuda.synchronize()
+    ref = oracle.blockdiag_attn(q, k, v, ids, lay.seq_start, scale, lay.enable_gqa)
+    qpos = np.arange(lay.seq_start, lay.seq_start + lay.L)
+    pad = torch.as_tensor(np.asarray(ids)[:, qpos] == oracle.PAD_DOC_ID)
+    return compare(out, ref, pad.unsqueeze(1).expand(lay.B, lay.Hq, lay.L), lay.name)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("regime", ["wide", "growing", "far_below"])
+def test_extreme_score_ranges(psb, D, regime):
+    # The kernel keeps an exp2 offset per row and moves it only when a lane's P for a tile
+    # sums past 2^8, starting from FLT_MAX so that a row's first keys set it.  These inputs
+    # drive that logic hard; the fp64 oracle is exact for them.
+    #   wide:      q and k scaled by 6 at scale 1: scores of magnitude in the hundreds, the
+    #              softmax close to one-hot, most weights far below fp32 range;
+    #   growing:   key j scaled by 1 + j / 40: each later tile's scores outgrow the offset,
+    #              so it moves on most tiles;
+    #   far_below: q . k near -500 for every pair: with an offset that started at 0 every
+    #              weight would underflow.
+    lay = random_layout(1300 + D, B=1, S=900, L=None, seq_start=0, Hq=4, Hkv=2, D=D, max_doc=400, max_pad=30)
+    q, k, v = make_qkv(lay, seed_base=7100 + D)
+    say(regime, "D", D, "S", lay.S)
+    if regime == "wide":
+        q = (q.float() * 6).to(torch.bfloat16)
+        k = (k.float() * 6).to(torch.bfloat16)
+        scale = 1.0
+    elif regime == "growing":
+        grow = 1.0 + torch.arange(lay.S, dtype=torch.float32) / 40.0
+        k = (k.float() * grow[None, None, :, None]).to(torch.bfloat16)
+        scale = 1.0
+    else:
+        q = torch.full_like(q, 2.0)
+        k = (torch.full_like(k, -2.0).float() + 0.05 * k.float()).to(torch.bfloat16)
+        scale = 1.0
+    mx, mean = _run_qkv(psb, lay, q, k, v, scale)
+    say(regime, "max/mean abs err", mx, mean)
