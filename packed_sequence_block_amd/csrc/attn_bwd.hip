@@ -178,9 +178,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     const int32_t ntiles = (thi - tlo + kKeysPerTile - 1) / kKeysPerTile;
     const __bf16* kbase = p.k + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
     const __bf16* vbase = p.v + ((int64_t)b * p.Hkv + g) * p.kv_len * D;
-    auto rsrc = [&](const __bf16* base, int32_t kt) {
+    // num_records 0 (on == false) turns every lane of a load into a zero fill with no memory
+    // access: the last tile issues such loads into the free stages
+    auto rsrc = [&](const __bf16* base, int32_t kt, bool on = true) {
       return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)(kt - p.kv_start) * D), (short)0,
-                                               min(thi - kt, kKeysPerTile) * row_bytes, kBufferFlags);
+                                               on ? min(thi - kt, kKeysPerTile) * row_bytes : 0, kBufferFlags);
     };
     auto issue_k = [&](__bf16* buf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t r = rsrc(kbase, kt);
@@ -258,19 +260,44 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero16;
 
-    // one 32-key half kb of the tile in kbuf / vbuf
-    auto half = [&](const __bf16* kbuf, const __bf16* vbuf, int32_t kt, int kb) {
+    // one 32-key half kb of the tile in kbuf / vbuf; half 0 also issues the next tile's
+    // loads (K segments, then V), one after each k-step's pair of MFMAs: issued as one burst
+    // they queue behind each other
+    constexpr int NLOAD = KSEG_ITERS + VSEG_ITERS;
+    auto half = [&](const __bf16* kbuf, const __bf16* vbuf, int32_t kt, int kb, __amdgpu_buffer_rsrc_t rkn,
+                    __bf16* kn, __amdgpu_buffer_rsrc_t rvn, __bf16* vn) {
       // S^T and dP^T for keys 32 kb .. 32 kb + 31
       floatx16 s = zero16, dp = zero16;
       const char* kp = (const char*)kbuf + 32 * KROWB * kb;
       const __bf16* vp = vbuf + v_rd + 32 * VROW * kb;
+      auto next_load = [&](int n) {
+        if (n < KSEG_ITERS) {
+          buffer_load_lds16(rkn, kn + (n * kBwdWaves + wv) * 512, koff[n]);
+        } else {
+          const int seg = (n - KSEG_ITERS) * kBwdWaves + wv;
+          if (VSEGS % kBwdWaves == 0 || seg < VSEGS) buffer_load_lds16(rvn, vn + seg * 512, voff[n - KSEG_ITERS]);
+        }
+      };
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
         const bf16x8 c = *(const bf16x8*)(vp + 16 * ks);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, oreg[ks], dp, 0, 0, 0);
+        if (kb == 0 && ks < NLOAD) next_load(ks);
       }
+      if (kb == 0) {
+#pragma unroll
+        for (int n = KS; n < NLOAD; ++n) next_load(n);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (ks < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
       const int32_t e = kt + 32 * kb + 4 * h - kshift;
       bf16x8 dsk[2];
@@ -324,12 +351,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       const int32_t kt = tlo + t * kKeysPerTile;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (t + 1 < ntiles) {
-        issue_k(kn, kt + kKeysPerTile);
-        issue_v(vn, kt + kKeysPerTile);
-      }
-      half(kc, vc, kt, 0);
-      half(kc, vc, kt, 1);
+      const bool more = t + 1 < ntiles;
+      const __amdgpu_buffer_rsrc_t rkn = rsrc(kbase, kt + kKeysPerTile, more);
+      const __amdgpu_buffer_rsrc_t rvn = rsrc(vbase, kt + kKeysPerTile, more);
+      half(kc, vc, kt, 0, rkn, kn, rvn, vn);
+      half(kc, vc, kt, 1, rkn, kn, rvn, vn);
     };
     int32_t t = 0;
     for (; t + 1 < ntiles; t += 2) {
