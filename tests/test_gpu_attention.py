@@ -167,3 +167,12 @@ def test_extreme_score_ranges(psb, D, regime):
         scale = 1.0
     mx, mean = _run_qkv(psb, lay, q, k, v, scale)
     say(regime, "max/mean abs err", mx, mean)
+
+
+@pytest.mark.parametrize("scale", [None, -0.3])
+def test_many_items_d128(psb, scale):
+    # a grid of several rounds of items per workgroup slot (6 x 64 row tiles x 8 head units =
+    # 3072 items) with random documents and padding tails, at D = 128
+    lay = random_layout(1500, B=6, S=2048, L=None, seq_start=0, Hq=32, Hkv=8, D=128, max_doc=700, max_pad=90)
+    mx, mean = run_case(psb, lay, seed_base=7600, scale=scale)
+    say("many items D128 scale", scale, "max/mean abs err", mx, mean)
