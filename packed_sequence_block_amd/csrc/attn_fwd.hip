@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
   // gives exp2(-inf) = 0; with sc = 0 it would give exp2(-inf * 0) = NaN.
   const float sc = fmaxf(neg ? -p.sc : p.sc, FLT_MIN);
   const floatx16 zero16 = {};
-  const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
+  [[maybe_unused]] const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
 
   // K and V loads: lane `lane` of segment seg fills 16-byte slot seg*64 + lane of the
   // tile, i.e. row slot / NCH at stored chunk slot % NCH, which holds global chunk
@@ -409,8 +409,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         }
       }
     };
-    // P = exp2(s sc + nmsc) as bf16 for 16-key step j; acc += its sum in this lane (of the
-    // bf16 values P V uses)
+    // P = exp2(s sc + nmsc) as bf16 for 16-key step j; acc += its sum in this lane.  The
+    // plan path sums the fp32 values with plain adds: v_dot2c_f32_bf16 (a sum of the bf16
+    // pair) does not issue while another wave's MFMA runs, and stalls this wave's in-order
+    // VALU work behind it, where adds co-execute.  The explicit-mask variant, one mask
+    // register set fuller, keeps the bf16 sum by v_dot2c, which needs no fp32 value live.
     auto softmax_step = [&](const floatx16 (&s)[2], int j, bf16x8& pj, float& acc) {
       bf16x2 pp[4];
 #pragma unroll
@@ -418,7 +421,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t], sc, nmsc));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][8 * (j & 1) + 2 * t + 1], sc, nmsc));
         pp[t] = cvt_bf16x2(e0, e1);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, acc, false);
+        if constexpr (DENSE)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones2, acc, false);
+        else
+          acc += e0 + e1;
       }
       pj = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                    __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);

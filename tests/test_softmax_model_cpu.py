@@ -4,15 +4,16 @@ The forward kernel walks 64-key tiles and keeps, per query row, an exp2 offset n
 a running sum l and an fp32 accumulator o (online softmax in the exp2 domain with
 sc = |scale| * log2(e)):
   * masked scores become -inf;
-  * p = exp2(s sc + nmsc) (one fused multiply-add), rounded to bf16, for the whole tile;
-  * if the bf16 p held by one lane (half of the tile's keys: key % 8 < 4, or the rest)
-    sum to more than 2^8, the offset is retuned: with m the tile's maximum raw score,
+  * e = exp2(s sc + nmsc) (one fused multiply-add) in fp32 for the whole tile, and
+    p = e rounded to bf16;
+  * if the e held by one lane (half of the tile's keys: key % 8 < 4, or the rest) sum
+    to more than 2^8, the offset is retuned: with m the tile's maximum raw score,
     nmsc' = -m sc replaces nmsc wherever it is smaller; l and o are multiplied by
-    exp2(nmsc' - nmsc) and the tile's p are recomputed;
+    exp2(nmsc' - nmsc) and the tile's e and p are recomputed;
   * nmsc starts at FLT_MAX, so that a row's first finite score gives p = inf and forces
     the exact maximum (masked scores still give exp2(-inf) = 0);
-  * l adds the bf16 p, o adds p times v; the output is o / l (0 when l == 0), rounded
-    to bf16.
+  * l adds the fp32 e, o adds the bf16 p times v; the output is o / l (0 when
+    l == 0), rounded to bf16.
 A negative scale flips the sign of q; sc is held at least at the smallest normal
 float, so that scale = 0 gives equal weights instead of exp2(-inf * 0) = NaN on the
 masked keys.  This model runs the same steps in numpy float32 (the MFMA dot products
@@ -60,16 +61,17 @@ def model_row(qrow, keys, vals, allowed, scale, clamp=True):
         for t0 in range(0, keys.shape[0], TILE):
             s = np.where(allowed[t0:t0 + TILE], s_all[t0:t0 + TILE], np.float32(-np.inf)).astype(np.float32)
             lane = (np.arange(t0, t0 + len(s)) % 8) < 4
-            p = _bf16(np.exp2(_fma32(s, sc, nmsc)))
-            if p[lane].sum(dtype=np.float32) > RETUNE_SUM or p[~lane].sum(dtype=np.float32) > RETUNE_SUM:
+            e = np.exp2(_fma32(s, sc, nmsc)).astype(np.float32)
+            if e[lane].sum(dtype=np.float32) > RETUNE_SUM or e[~lane].sum(dtype=np.float32) > RETUNE_SUM:
                 nm = np.float32(-np.float32(s.max()) * sc)
                 if nm < nmsc:
                     alpha = np.float32(np.exp2(np.float32(nm - nmsc)))
                     nmsc = nm
                     l = np.float32(l * alpha)
                     o = (o * alpha).astype(np.float32)
-                p = _bf16(np.exp2(_fma32(s, sc, nmsc)))
-            l = np.float32(l + p.sum(dtype=np.float32))
+                e = np.exp2(_fma32(s, sc, nmsc)).astype(np.float32)
+            p = _bf16(e)
+            l = np.float32(l + e.sum(dtype=np.float32))
             o = (o + p @ vals[t0:t0 + TILE].astype(np.float32)).astype(np.float32)
     inv = np.float32(1.0) / l if l > 0 else np.float32(0.0)
     return _bf16(o * inv)
