@@ -278,11 +278,24 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
           if (VSEGS % kBwdWaves == 0 || seg < VSEGS) buffer_load_lds16(rvn, vn + seg * 512, voff[n - KSEG_ITERS]);
         }
       };
+      // K and V operands read AH k-steps ahead of their MFMAs (pinned below: issued one
+      // pair at a time right before its MFMAs, each read would hold its MFMA for the whole
+      // LDS latency)
+      constexpr int AH = (KS < 2) ? KS : 2;
       __builtin_amdgcn_sched_barrier(0);
+      bf16x8 ar[AH], cr[AH];
+#pragma unroll
+      for (int ks = 0; ks < AH; ++ks) {
+        ar[ks] = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
+        cr[ks] = *(const bf16x8*)(vp + 16 * ks);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
-        const bf16x8 c = *(const bf16x8*)(vp + 16 * ks);
+        const bf16x8 a = ar[ks % AH], c = cr[ks % AH];
+        if (ks + AH < KS) {
+          ar[ks % AH] = *(const bf16x8*)(kp + (k_rd ^ (32 * (ks + AH))));
+          cr[ks % AH] = *(const bf16x8*)(vp + 16 * (ks + AH));
+        }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, oreg[ks], dp, 0, 0, 0);
         if (kb == 0 && ks < NLOAD) next_load(ks);
@@ -290,12 +303,22 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       if (kb == 0) {
 #pragma unroll
         for (int n = KS; n < NLOAD; ++n) next_load(n);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          if (ks < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (ks + AH < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (kb == 0 && ks < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the first dQ step's K^T operands, read under the dS VALU work below
+      bf16x8 ta[DB];
+      {
+        const char* tp = (const char*)kbuf + 32 * kb * KROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          ta[db] = vtr_pair_at(tp + (kt_rd ^ (64 * db)), tp + 8 * KROWB + (kt_rd ^ (64 * db + 32)));
       }
       __builtin_amdgcn_sched_barrier(0);
       const bool full = single && kt >= w_lo && (kt + 63) <= wq0;
@@ -332,16 +355,26 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
       };
       if (full) ds_step(std::false_type{});
       else ds_step(std::true_type{});
-      // dQ^T += K^T dS^T over the two 16-key steps of this half
+      // dQ^T += K^T dS^T over the two 16-key steps of this half, the second step's operands
+      // read one step ahead
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const char* tp = (const char*)kbuf + (32 * kb + 16 * j) * KROWB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = vtr_pair_at(tp + (kt_rd ^ (64 * db)), tp + 8 * KROWB + (kt_rd ^ (64 * db + 32)));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsk[j], acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], dsk[j], acc[db], 0, 0, 0);
+          if (j == 0) {
+            const char* tp = (const char*)kbuf + (32 * kb + 16) * KROWB;
+            ta[db] = vtr_pair_at(tp + (kt_rd ^ (64 * db)), tp + 8 * KROWB + (kt_rd ^ (64 * db + 32)));
+          }
         }
       }
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     __syncthreads();  // the previous item no longer reads LDS
