@@ -757,19 +757,32 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
       // dV^T += dO^T P and dK^T += Q^T dS over the 16-row k-steps
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) {
+        // operands read two MFMA pairs ahead (pinned below): issued one pair at a time right
+        // before their MFMAs, each pair would hold its MFMAs for the whole LDS latency
+        auto opnd = [&](const __bf16* base, int i) {
+          const char* tp = (const char*)base + (32 * hf + 16 * (i / DB)) * QROWB;
+          const int db = i % DB;
+          return vtr_pair_at(tp + (t_rd ^ (64 * db)), tp + 8 * QROWB + (t_rd ^ (64 * db + 32)));
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ro[2], rq[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const char* to = (const char*)ob + (32 * hf + 16 * j) * QROWB;
-          const char* tq = (const char*)qb + (32 * hf + 16 * j) * QROWB;
+        for (int i = 0; i < 2; ++i) { ro[i] = opnd(ob, i); rq[i] = opnd(qb, i); }
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int t0 = t_rd ^ (64 * db), t1 = 8 * QROWB + (t_rd ^ (64 * db + 32));
-            const bf16x8 ao = vtr_pair_at(to + t0, to + t1);
-            const bf16x8 aq = vtr_pair_at(tq + t0, tq + t1);
-            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pk[hf][j], dva[db], 0, 0, 0);
-            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsk[hf][j], dka[db], 0, 0, 0);
-          }
+        for (int i = 0; i < 2 * DB; ++i) {
+          const int j = i / DB, db = i % DB;
+          const bf16x8 co = ro[i & 1], cq = rq[i & 1];
+          if (i + 2 < 2 * DB) { ro[i & 1] = opnd(ob, i + 2); rq[i & 1] = opnd(qb, i + 2); }
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(co, pk[hf][j], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cq, dsk[hf][j], dka[db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (i + 2 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
