@@ -658,22 +658,62 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
       floatx16 s[NHALF], dp[NHALF];
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) { s[hf] = zero16; dp[hf] = zero16; }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int hf = 0; hf < NHALF; ++hf) {
-          const bf16x8 aq = *(const bf16x8*)((const char*)qb + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
-          const bf16x8 ao = *(const bf16x8*)((const char*)ob + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
-          s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
-          const bf16x8 bv = VLDS ? *(const bf16x8*)(sV + v_rd + 16 * ks) : vreg[ks];
-          dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, dp[hf], 0, 0, 0);
-        }
-        constexpr int EVERY = (KS / QFULL >= 1) ? KS / QFULL : 1;
+      constexpr int EVERY = (KS / QFULL >= 1) ? KS / QFULL : 1;
+      auto spread_load = [&](int ks) {
         if (SPREAD && (ks % EVERY) == EVERY - 1 && ks / EVERY < QFULL) {
           const int j = ks / EVERY;
           const int seg = j * kBwdWaves + wv;
           buffer_load_lds16(rn.q, qn + seg * 512, qoff[j]);
           buffer_load_lds16(rn.o, on + seg * 512, qoff[j]);
+        }
+      };
+      if constexpr (D == 64) {
+        // Q / dO operands read two k-steps ahead of their MFMAs, pinned below (V is in
+        // VGPRs at D = 64; at D = 128 a ring of Q, dO and V operands spills 13 more registers)
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 rq[2][NHALF], ro[2][NHALF];
+        auto rd = [&](int ks, int hf, bf16x8& aq, bf16x8& ao) {
+          aq = *(const bf16x8*)((const char*)qb + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
+          ao = *(const bf16x8*)((const char*)ob + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
+        };
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int hf = 0; hf < NHALF; ++hf) rd(ks, hf, rq[ks][hf], ro[ks][hf]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int hf = 0; hf < NHALF; ++hf) {
+            const bf16x8 aq = rq[ks & 1][hf], ao = ro[ks & 1][hf];
+            if (ks + 2 < KS) rd(ks + 2, hf, rq[ks & 1][hf], ro[ks & 1][hf]);
+            s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
+            dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[ks], dp[hf], 0, 0, 0);
+          }
+          spread_load(ks);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NHALF, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int hf = 0; hf < NHALF; ++hf) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          if (SPREAD && (ks % EVERY) == EVERY - 1 && ks / EVERY < QFULL) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int hf = 0; hf < NHALF; ++hf) {
+            const bf16x8 aq = *(const bf16x8*)((const char*)qb + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
+            const bf16x8 ao = *(const bf16x8*)((const char*)ob + 32 * hf * QROWB + (a_rd ^ (32 * ks)));
+            s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[ks], s[hf], 0, 0, 0);
+            const bf16x8 bv = VLDS ? *(const bf16x8*)(sV + v_rd + 16 * ks) : vreg[ks];
+            dp[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, dp[hf], 0, 0, 0);
+          }
+          spread_load(ks);
         }
       }
       if constexpr (SPREAD && KS / QFULL < 1) {
