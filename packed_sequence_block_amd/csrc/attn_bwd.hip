@@ -41,11 +41,6 @@ namespace psb {
 namespace {
 
 constexpr int kBwdWaves = 4;
-// LDS row padding (elements) of a tile read only row-wise (ds_read_b128): a pitch of 16
-// bytes mod 256 has no bank conflicts.  A tile also read through transposing reads needs
-// 64 bytes mod 256 there, so no pitch serves both: such tiles (K in dq, Q and dO in dk/dv)
-// are swizzled instead (tile_swz).
-constexpr int DQ_KPAD = 8;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 constexpr int kKeysPerWave = 32;                       // dkdv: keys per wave
 constexpr int kKeysPerItem = kKeysPerWave * kBwdWaves; // dkdv: keys per workgroup
@@ -94,19 +89,15 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NCH = D / 8;
-  // K is read row-wise (S^T = K Q^T) and transposed (dQ^T += K^T dS^T): a swizzled tile
-  // of unpadded rows (tile_swz).  V is only read row-wise: rows padded to D + 8.
+  // K is read row-wise (S^T = K Q^T) and transposed (dQ^T += K^T dS^T), V row-wise only
+  // (dP^T = V dO^T): both are swizzled tiles of unpadded rows (tile_swz), read row-wise at
+  // the same addresses.
   constexpr int KROWB = D * 2;                            // K tile row, bytes
   constexpr int KSTAGE = kKeysPerTile * D;
   constexpr int KSEGS = kKeysPerTile * NCH / 64;
   constexpr int KSEG_ITERS = KSEGS / kBwdWaves;
-  constexpr int VROW = D + DQ_KPAD;                       // padded V tile row
-  constexpr int VCH = VROW / 8;                           // 16-byte slots per row
-  constexpr int VSTAGE = kKeysPerTile * VROW;
-  constexpr int VSEGS = kKeysPerTile * VCH / 64;
-  constexpr int VSEG_ITERS = (VSEGS + kBwdWaves - 1) / kBwdWaves;
-  static_assert(KSEGS % kBwdWaves == 0 && KSTAGE * 2 == KSEGS * 1024, "K tile segments");
-  static_assert(VSEGS * 64 == kKeysPerTile * VCH && VSTAGE * 2 == VSEGS * 1024, "V tile segments");
+  constexpr int VSTAGE = KSTAGE;
+  static_assert(KSEGS % kBwdWaves == 0 && KSTAGE * 2 == KSEGS * 1024, "K / V tile segments");
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[KSTAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[VSTAGE];
@@ -120,8 +111,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
   const float sc = p.sc;  // |scale| * log2(e); Q is sign-flipped for a negative scale
   const floatx16 zero16 = {};
 
-  // slot seg * 64 + lane of a K tile holds row slot / NCH, stored chunk slot % NCH, which is
-  // global chunk (stored chunk) ^ tile_swz(row); V slots are row-major with pad slots
+  // slot seg * 64 + lane of a K or V tile holds row slot / NCH, stored chunk slot % NCH,
+  // which is global chunk (stored chunk) ^ tile_swz(row)
   int32_t koff[KSEG_ITERS];
 #pragma unroll
   for (int j = 0; j < KSEG_ITERS; ++j) {
@@ -129,17 +120,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     const int row = slot / NCH, pc = slot % NCH;
     koff[j] = row * row_bytes + 16 * (pc ^ tile_swz<D>(row));
   }
-  int32_t voff[VSEG_ITERS];
-#pragma unroll
-  for (int j = 0; j < VSEG_ITERS; ++j) {
-    const int slot = (j * kBwdWaves + wv) * 64 + lane;
-    const int row = slot / VCH, ch = slot % VCH;
-    voff[j] = (ch < NCH) ? row * row_bytes + 16 * ch : 0x7ffffff0;
-  }
-  // A = K rows, byte address: k-step ks reads chunk 2 ks + h of row lr, stored at
-  // k_rd ^ (32 ks) (the chunk bits and the row bits never overlap)
+  // A = K rows (and V rows), byte address: k-step ks reads chunk 2 ks + h of row lr, stored
+  // at k_rd ^ (32 ks) (the chunk bits and the row bits never overlap)
   const int k_rd = lr * KROWB + 16 * (h ^ tile_swz<D>(lr));
-  const int v_rd = lr * VROW + 8 * h;  // A = V rows, element index
   // transposing read of K^T: key r0 = 4 h + (lane & 15) / 4 (+ 16 j + 32 kb, + 8 for the
   // pair's second read), d bytes 64 db + 32 ((lane >> 4) & 1) + 8 (lane & 3); stored at
   // kt_rd ^ (64 db) (second read: ^ 32, 8 rows on)
@@ -192,10 +175,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     auto issue_v = [&](__bf16* buf, int32_t kt) {
       const __amdgpu_buffer_rsrc_t r = rsrc(vbase, kt);
 #pragma unroll
-      for (int j = 0; j < VSEG_ITERS; ++j) {
-        const int seg = j * kBwdWaves + wv;
-        if (VSEGS % kBwdWaves == 0 || seg < VSEGS) buffer_load_lds16(r, buf + seg * 512, voff[j]);
-      }
+      for (int j = 0; j < KSEG_ITERS; ++j) buffer_load_lds16(r, buf + (j * kBwdWaves + wv) * 512, koff[j]);
     };
 
     // ---- per-wave rows: document range (as in the forward) --------------------------
@@ -263,20 +243,18 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
     // one 32-key half kb of the tile in kbuf / vbuf; half 0 also issues the next tile's
     // loads (K segments, then V), one after each k-step's pair of MFMAs: issued as one burst
     // they queue behind each other
-    constexpr int NLOAD = KSEG_ITERS + VSEG_ITERS;
+    constexpr int NLOAD = 2 * KSEG_ITERS;
     auto half = [&](const __bf16* kbuf, const __bf16* vbuf, int32_t kt, int kb, __amdgpu_buffer_rsrc_t rkn,
                     __bf16* kn, __amdgpu_buffer_rsrc_t rvn, __bf16* vn) {
       // S^T and dP^T for keys 32 kb .. 32 kb + 31
       floatx16 s = zero16, dp = zero16;
       const char* kp = (const char*)kbuf + 32 * KROWB * kb;
-      const __bf16* vp = vbuf + v_rd + 32 * VROW * kb;
+      const char* vp = (const char*)vbuf + 32 * KROWB * kb;
       auto next_load = [&](int n) {
-        if (n < KSEG_ITERS) {
+        if (n < KSEG_ITERS)
           buffer_load_lds16(rkn, kn + (n * kBwdWaves + wv) * 512, koff[n]);
-        } else {
-          const int seg = (n - KSEG_ITERS) * kBwdWaves + wv;
-          if (VSEGS % kBwdWaves == 0 || seg < VSEGS) buffer_load_lds16(rvn, vn + seg * 512, voff[n - KSEG_ITERS]);
-        }
+        else
+          buffer_load_lds16(rvn, vn + ((n - KSEG_ITERS) * kBwdWaves + wv) * 512, koff[n - KSEG_ITERS]);
       };
       // K and V operands read AH k-steps ahead of their MFMAs (pinned below: issued one
       // pair at a time right before its MFMAs, each read would hold its MFMA for the whole
@@ -287,14 +265,14 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dq_kernel(BwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < AH; ++ks) {
         ar[ks] = *(const bf16x8*)(kp + (k_rd ^ (32 * ks)));
-        cr[ks] = *(const bf16x8*)(vp + 16 * ks);
+        cr[ks] = *(const bf16x8*)(vp + (k_rd ^ (32 * ks)));
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = ar[ks % AH], c = cr[ks % AH];
         if (ks + AH < KS) {
           ar[ks % AH] = *(const bf16x8*)(kp + (k_rd ^ (32 * (ks + AH))));
-          cr[ks % AH] = *(const bf16x8*)(vp + 16 * (ks + AH));
+          cr[ks % AH] = *(const bf16x8*)(vp + (k_rd ^ (32 * (ks + AH))));
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, oreg[ks], dp, 0, 0, 0);
