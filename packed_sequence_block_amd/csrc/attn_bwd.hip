@@ -563,13 +563,20 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
     const int32_t nsteps_h = (wg_hi > wg_lo) ? (wg_hi - wg_lo + kRowsPerStep - 1) / kRowsPerStep : 0;
     float pend_l = 0.f, pend_d = 0.f;
     const int32_t nsteps = nsteps_h * p.group;
+    // Step st covers query head hh = st / nsteps_h of the group and the kRowsPerStep rows
+    // from wg_lo + kRowsPerStep ri, ri = st % nsteps_h.  The steps run in order, so (hh, ri) is carried from step to step
+    // instead of divided out (a runtime division is some 40 scalar instructions).
+    struct StepPos { int32_t hh, ri; };
+    auto advance = [&](StepPos s) {
+      if (++s.ri == nsteps_h) { s.ri = 0; ++s.hh; }
+      return s;
+    };
     // buffer resources of step st's Q and dO rows; a step past the last gets zero records,
     // so its loads become zero fills of the free stage with no memory access
     struct StepRsrc { __amdgpu_buffer_rsrc_t q, o; };
-    auto step_rsrc = [&](int32_t st) {
+    auto step_rsrc = [&](int32_t st, StepPos sp) {
       const bool on = st < nsteps;
-      const int32_t sst = on ? st : 0;
-      const int32_t hh = sst / nsteps_h, rr = wg_lo + (sst % nsteps_h) * kRowsPerStep;
+      const int32_t hh = on ? sp.hh : 0, rr = wg_lo + (on ? sp.ri : 0) * kRowsPerStep;
       const int32_t hq = g * p.group + hh;
       const int64_t base = ((int64_t)b * p.Hq + hq) * p.L + rr;
       const int32_t nrows = on ? min(kRowsPerStep, p.L - rr) : 0;
@@ -595,8 +602,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
     };
     // the step's row lse / delta go to registers now and to LDS at the step's start,
     // after the wait that the tile loads need anyway
-    auto issue_rows = [&](int32_t st) {
-      const int32_t hh = st / nsteps_h, rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
+    auto issue_rows = [&](StepPos sp) {
+      const int32_t hh = sp.hh, rr = wg_lo + sp.ri * kRowsPerStep;
       const int32_t hq = g * p.group + hh;
       const int64_t base = ((int64_t)b * p.Hq + hq) * p.L + rr;
       const int32_t nrows = min(kRowsPerStep, p.L - rr);
@@ -607,12 +614,12 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
         pend_d = in ? p.delta[base + tid] : 0.f;
       }
     };
-    auto issue = [&](int32_t st, __bf16* qb, __bf16* ob) {
-      const StepRsrc r = step_rsrc(st);
+    auto issue = [&](int32_t st, StepPos sp, __bf16* qb, __bf16* ob) {
+      const StepRsrc r = step_rsrc(st, sp);
 #pragma unroll
       for (int j = 0; j < QFULL; ++j) issue_seg(r, qb, ob, j);
       issue_rest(r, qb, ob);
-      issue_rows(st);
+      issue_rows(sp);
     };
 
     // one step: kRowsPerStep rows as NHALF independent 32-row halves, so the MFMAs of one
@@ -621,9 +628,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
     // the next step's full-round segments are issued inside the first MFMA loop, one every
     // KS / QFULL k-steps, alternating Q and dO (a wave with nothing to compute issues them
     // at once)
-    auto compute = [&](int32_t st, const __bf16* qb, const __bf16* ob, int stage, const StepRsrc& rn, __bf16* qn,
+    auto compute = [&](StepPos sp, const __bf16* qb, const __bf16* ob, int stage, const StepRsrc& rn, __bf16* qn,
                        __bf16* on) {
-      const int32_t rr = wg_lo + (st % nsteps_h) * kRowsPerStep;
+      const int32_t rr = wg_lo + sp.ri * kRowsPerStep;
       // rows of this step that this wave's keys can see at all
       if (rr >= w_hi || rr + kRowsPerStep <= w_lo) {
         if constexpr (SPREAD) {
@@ -805,19 +812,22 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
     };
 
     __syncthreads();  // the previous item no longer reads LDS (and s_rng is read)
-    if (nsteps > 0) issue(0, sQ0, sO0);
+    StepPos cur = {0, 0};  // position of step st in the loop below
+    if (nsteps > 0) issue(0, cur, sQ0, sO0);
     auto step = [&](int32_t st, const __bf16* qc, const __bf16* oc, __bf16* qn, __bf16* on, int stage) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (tid < kRowsPerStep) { sL[stage][tid] = pend_l; sDl[stage][tid] = pend_d; }
       __syncthreads();
-      const StepRsrc rn = step_rsrc(st + 1);
+      const StepPos nxt = advance(cur);
+      const StepRsrc rn = step_rsrc(st + 1, nxt);
       if constexpr (!SPREAD) {
 #pragma unroll
         for (int j = 0; j < QFULL; ++j) issue_seg(rn, qn, on, j);
       }
       issue_rest(rn, qn, on);
-      if (st + 1 < nsteps) issue_rows(st + 1);
-      compute(st, qc, oc, stage, rn, qn, on);
+      if (st + 1 < nsteps) issue_rows(nxt);
+      compute(cur, qc, oc, stage, rn, qn, on);
+      cur = nxt;
     };
     int32_t st = 0;
     for (; st + 1 < nsteps; st += 2) {
