@@ -708,6 +708,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
       bf16x8 pk[NHALF][2], dsk[NHALF][2];
       // P and dS; a step whose rows all see every key of the wave takes the copy without the
       // per-row test (wave-uniform condition)
+      // row r = rr + 32 hf + 8 a + 4 h + c of the step is one of the key's rows iff
+      // r - r_lo = rbase + (32 hf + 8 a + c) < kspan (unsigned); rbase is opaque so that each
+      // test stays one add of a constant (the compiler otherwise rebuilds r - r_lo per pair)
+      uint32_t rbase = (uint32_t)(rr + 4 * h - r_lo);
+      asm volatile("" : "+v"(rbase));
       auto p_ds = [&](auto masked) {
 #pragma unroll
         for (int hf = 0; hf < NHALF; ++hf) {
@@ -726,8 +731,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
                 const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
                 float pr;
                 if constexpr (decltype(masked)::value) {
-                  const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
-                  pr = ((uint32_t)(r - r_lo) < kspan) ? __builtin_amdgcn_exp2f(arg) : 0.f;
+                  const bool ok = rbase + (uint32_t)(32 * hf + 8 * a + c + u) < kspan;
+                  pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
                 } else {
                   pr = __builtin_amdgcn_exp2f(arg);
                 }
@@ -763,8 +768,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
                 const int i = 4 * a + c + u;
-                const int32_t r = rr + 32 * hf + 8 * a + 4 * h + c + u;
-                const bool ok = (uint32_t)(r - r_lo) < kspan;
+                const bool ok = rbase + (uint32_t)(32 * hf + 8 * a + c + u) < kspan;
                 const float arg = __builtin_fmaf(s[hf][i], ssc, -lv[c + u]);  // Q is not sign-flipped here
                 const float pr = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
                 pp[u] = pr;
