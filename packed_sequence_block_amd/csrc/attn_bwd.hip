@@ -866,43 +866,52 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dkdv_kernel(BwdParams p) {
 }
 
 // ---- dK, dV of split key tiles: the chunks' partials summed in chunk order -------------
-// Workgroup = (split tile, kv head), the dK / dV kernel's lane layout; grid covers the most
-// split tiles a plan can make, the rest exit.
+// Workgroup = (split tile, kv head, 32-wide d block), the dK / dV kernel's lane layout; the
+// grid covers the most split tiles a plan can make, the rest exit.  Chunk j + 1's partials
+// are loaded before chunk j's are added, so consecutive chunks' loads overlap while the sum
+// keeps chunk order.
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads) dkdv_reduce_kernel(BwdParams p) {
   constexpr int DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, lr = lane & 31;
-  const int32_t i = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+  const int32_t db = blockIdx.x % DB, tg = blockIdx.x / DB;
+  const int32_t i = tg / p.Hkv, g = tg % p.Hkv;
   if (i >= *p.split_n) return;
   const int32_t b = p.split[4 * i], kt_i = p.split[4 * i + 1], slot0 = p.split[4 * i + 2], n = p.split[4 * i + 3];
   if (b < 0 || b >= p.B || kt_i < 0 || slot0 < 0 || n < 2 || n > p.max_slots || slot0 > p.max_slots - n) return;
-  floatx16 dka[DB], dva[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) { dka[db] = floatx16{}; dva[db] = floatx16{}; }
-  for (int32_t j = 0; j < n; ++j) {
+  floatx16 dka = {}, dva = {};
+  float4 a[2][4], c[2][4];
+  auto load = [&](int32_t j, float4 (&aa)[4], float4 (&cc)[4]) {
     const float4* pp = partial_at<D>(p.partial, slot0 + j, p.Hkv, g, wv);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      aa[i4] = pp[((0 * DB + db) * 4 + i4) * 64 + lane];
+      cc[i4] = pp[((1 * DB + db) * 4 + i4) * 64 + lane];
+    }
+  };
+  auto add = [&](const float4 (&aa)[4], const float4 (&cc)[4]) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 a = pp[((0 * DB + db) * 4 + i4) * 64 + lane];
-        const float4 c = pp[((1 * DB + db) * 4 + i4) * 64 + lane];
-        dka[db][4 * i4] += a.x; dka[db][4 * i4 + 1] += a.y; dka[db][4 * i4 + 2] += a.z; dka[db][4 * i4 + 3] += a.w;
-        dva[db][4 * i4] += c.x; dva[db][4 * i4 + 1] += c.y; dva[db][4 * i4 + 2] += c.z; dva[db][4 * i4 + 3] += c.w;
-      }
+    for (int i4 = 0; i4 < 4; ++i4) {
+      dka[4 * i4] += aa[i4].x; dka[4 * i4 + 1] += aa[i4].y; dka[4 * i4 + 2] += aa[i4].z; dka[4 * i4 + 3] += aa[i4].w;
+      dva[4 * i4] += cc[i4].x; dva[4 * i4 + 1] += cc[i4].y; dva[4 * i4 + 2] += cc[i4].z; dva[4 * i4 + 3] += cc[i4].w;
+    }
+  };
+  load(0, a[0], c[0]);  // n >= 2
+  int32_t j = 0;
+  for (; j + 2 <= n; j += 2) {
+    load(j + 1, a[1], c[1]);
+    add(a[0], c[0]);
+    if (j + 2 < n) load(j + 2, a[0], c[0]);
+    add(a[1], c[1]);
   }
+  if (j < n) add(a[0], c[0]);
   const int32_t key = p.kv_start + kt_i * kKeysPerItem + kKeysPerWave * wv + lr;
   const bool key_in = key < p.kv_start + p.kv_len;
   const int64_t kvrow = ((int64_t)b * p.Hkv + g) * p.kv_len + (key - p.kv_start);
-  __bf16* dkr = p.dk + kvrow * D;
-  __bf16* dvr = p.dv + kvrow * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    store_block_bf16(dkr + 32 * db, dka[db], p.scale, key_in, h);
-    store_block_bf16(dvr + 32 * db, dva[db], 1.f, key_in, h);
-  }
+  store_block_bf16(p.dk + kvrow * D + 32 * db, dka, p.scale, key_in, h);
+  store_block_bf16(p.dv + kvrow * D + 32 * db, dva, 1.f, key_in, h);
 }
 
 int heads_per_wg_bwd(int64_t group) { return (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1); }
@@ -935,7 +944,7 @@ hipError_t launch_bwd(int nh, const BwdParams& prm, int64_t rows, hipStream_t s)
   dkdv_kernel<D><<<dim3((unsigned)kgrid), dim3(kBwdThreads), 0, s>>>(prm);
   e = hipGetLastError();
   if (e != hipSuccess || prm.max_slots < 2) return e;
-  dkdv_reduce_kernel<D><<<dim3((unsigned)(prm.max_slots / 2 * prm.Hkv)), dim3(kBwdThreads), 0, s>>>(prm);
+  dkdv_reduce_kernel<D><<<dim3((unsigned)(prm.max_slots / 2 * prm.Hkv * (D / 32))), dim3(kBwdThreads), 0, s>>>(prm);
   return hipGetLastError();
 }
 
