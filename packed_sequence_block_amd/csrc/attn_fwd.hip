@@ -455,12 +455,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
     // of the first step read meanwhile), one wave-uniform test of the lane sums, then the
     // P V MFMAs with the next step's V^T operands read one step ahead.  With two or three
     // waves per SIMD the other waves' exp2 work runs under these MFMAs.
-    auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf) {
+    // An item's first tile takes the tile's row max as its offset before any P is made: O
+    // and l are still 0 there, so this is what the rescale path would do (alpha = 0 at a
+    // row's first finite key) without making that tile's P twice and scaling O by 0.  A row
+    // with no key in the tile keeps nmsc = FLT_MAX (its max is -inf).
+    auto softmax_pv = [&](const floatx16 (&s)[2], const __bf16* vbuf, bool first) {
       const char* vb = (const char*)vbuf;
       bf16x8 pk[4];
       bf16x8 va[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) va[db] = vtr(vb, 0, db);
+      if (first) {
+        const float nm = -tile_max(s) * sc;
+        nmsc = (nm < nmsc) ? nm : nmsc;
+      }
       float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) softmax_step(s, j, pk[j], ls);
@@ -515,7 +523,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(AttnParams p) {
       if (more) load_mask(kt + kKeysPerTile, mnext);
       apply_mask(st_s, mcur);
       mask_tile(kt, st_s);
-      softmax_pv(st_s, vcur);
+      softmax_pv(st_s, vcur, t == 0);
     };
     int32_t t = 0;
     for (; t + 1 < ntiles; t += 2) {

@@ -10,8 +10,10 @@ sc = |scale| * log2(e)):
     to more than 2^8, the offset is retuned: with m the tile's maximum raw score,
     nmsc' = -m sc replaces nmsc wherever it is smaller; l and o are multiplied by
     exp2(nmsc' - nmsc) and the tile's e and p are recomputed;
-  * nmsc starts at FLT_MAX, so that a row's first finite score gives p = inf and forces
-    the exact maximum (masked scores still give exp2(-inf) = 0);
+  * on the first tile, nmsc' = -m sc is taken before any e is made (where smaller than
+    nmsc), which is what the retune does there with l and o still 0;
+  * nmsc starts at FLT_MAX, so that a row's first finite score in a later tile gives
+    p = inf and forces the exact maximum (masked scores still give exp2(-inf) = 0);
   * l adds the fp32 e, o adds the bf16 p times v; the output is o / l (0 when
     l == 0), rounded to bf16.
 A negative scale flips the sign of q; sc is held at least at the smallest normal
@@ -61,6 +63,9 @@ def model_row(qrow, keys, vals, allowed, scale, clamp=True):
         for t0 in range(0, keys.shape[0], TILE):
             s = np.where(allowed[t0:t0 + TILE], s_all[t0:t0 + TILE], np.float32(-np.inf)).astype(np.float32)
             lane = (np.arange(t0, t0 + len(s)) % 8) < 4
+            if t0 == 0:
+                nm = np.float32(-np.float32(s.max()) * sc)
+                nmsc = nm if nm < nmsc else nmsc
             e = np.exp2(_fma32(s, sc, nmsc)).astype(np.float32)
             if e[lane].sum(dtype=np.float32) > RETUNE_SUM or e[~lane].sum(dtype=np.float32) > RETUNE_SUM:
                 nm = np.float32(-np.float32(s.max()) * sc)
