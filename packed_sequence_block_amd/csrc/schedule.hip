@@ -237,15 +237,18 @@ __global__ void __launch_bounds__(256) key_range_kernel(const int32_t* __restric
 // Key-side plan (one workgroup): splits key tiles whose row range is far longer than a
 // workgroup slot's balanced share into row chunks and orders all records longest first.
 //   * W = total rows over all tiles; a record of r rows costs r x group per workgroup and
-//     there are B * nkt x Hkv workgroups' worth of records over kKeySlots concurrent slots
-//     (two workgroups on each of 256 CUs), so the chunk length is
-//     Rc = max(kMinChunkRows, W * Hkv / kKeySlots rounded up to 32 rows);
+//     there are B * nkt x Hkv workgroups' worth of records, so the chunk length is
+//     Rc = max(kMinChunkRows, W * Hkv / kKeySlots rounded up to 32 rows).  kKeySlots is
+//     three quarters of the concurrent slots (two workgroups on each of 256 CUs): chunks
+//     somewhat longer than a slot's even share split fewer tiles (less fp32 partial
+//     traffic) and leave the short records to fill the slots that finish early; 384 was
+//     faster than 256, 320, 448, 512 and 768 on the packed-row and shard workloads;
 //   * a tile of len > Rc rows would take n = ceil(len / Rc) chunks (at most kMaxChunks);
 //     partial slots go to the tiles with the most chunks first, as long as the slot budget
 //     lasts; a tile that gets none stays one record;
 //   * records are counting-sorted by ceil(rows / 64), descending.
 constexpr int kKeyPlanThreads = 1024;
-constexpr int kKeySlots = 512;
+constexpr int kKeySlots = 384;
 constexpr int kMinChunkRows = 256;
 constexpr int kMaxChunks = 16;
 
